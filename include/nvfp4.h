@@ -1,0 +1,203 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 linear-layer library.
+ *
+ * What it computes (sources: the web pages about arXiv 2609.04098, "Why Gated
+ * DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for the Recurrent Half of
+ * a Hybrid 27B LLM"):
+ *   - linear layers with 4-bit weights and 4-bit activations, "W4A4"
+ *     (bayesiansapien page, TL;DR), in NVIDIA's FP4 format NVFP4 (aipulsen
+ *     page, second paragraph);
+ *   - NVFP4 block scaling with one scale per 16 elements (bayesiansapien
+ *     page, "The four-part mechanism study", first item; nefut page, first
+ *     bullet);
+ *   - per-module global scales that a kernel fusing several modules into one
+ *     GEMM must apply module by module (bayesiansapien page, mechanism study,
+ *     "Two practical repairs"; nefut page, last paragraph; aimodeling page,
+ *     "What engineers should actually take away").
+ *
+ * Number format (standard NVFP4; the pages name only "NVFP4"):
+ *   element  E2M1, 4 bits (sign, 2 exponent bits, 1 mantissa bit, bias 1):
+ *            magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; two per byte, the LOW
+ *            nibble holds the even-indexed element.
+ *   scale    E4M3 ("FN", bias 7, max 448), one byte per 16 consecutive
+ *            elements along a row (the contraction axis of the GEMM).
+ *   global   one FP32 per tensor (per module for fused weights), stored in
+ *            encode form g = 2688 / amax (2688 = 6 * 448; g = 1 for amax 0).
+ *
+ * Quantisation of a 16-element block with maximum magnitude m (FP32, every
+ * step one correctly rounded operation):
+ *   u = min((m / 6) * g, 448); S = E4M3 round-to-nearest-even(u);
+ *   S == 0 -> all 16 codes are 0; else r = g / value(S) and
+ *   code_i = sign(x_i) << 3 | E2M1 round-to-nearest-even, saturating at 6, of |x_i * r|.
+ * Dequantised element = e2m1(code) * e4m3(S); the GEMM divides the product
+ * by g_a * g_w:  y[m][n] = sum_k a[m][k] w[n][k] / (g_a * g_w[segment of n]).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  bf16 tensors are
+ *     passed as uint16_t bit patterns.  All device buffers are owned and
+ *     allocated by the caller; the library allocates no device memory and
+ *     keeps no mutable global state (apart from a thread-local copy of the
+ *     last HIP error).  Host arrays are only read during the call.
+ *   - Work is enqueued on `stream` (0 = the null stream); no call
+ *     synchronises.  Device-side failures surface at the caller's next
+ *     synchronisation.
+ *   - Return value 0 = success, a negative NVFP4_E* code otherwise.  On a
+ *     validation error nothing is enqueued.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *   - Device pointers must be 16-byte aligned; leading dimensions are in
+ *     elements and must keep every row 16-byte aligned where noted.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
+
+/* Status codes. */
+#define NVFP4_OK 0
+#define NVFP4_EINVAL (-1)       /* null pointer, unknown enum value, bad count */
+#define NVFP4_ESHAPE (-2)       /* sizes that violate a stated shape rule */
+#define NVFP4_EALIGN (-3)       /* pointer or leading dimension not aligned */
+#define NVFP4_EUNSUPPORTED (-4) /* valid request outside what this build runs */
+#define NVFP4_EHIP (-5)         /* a HIP launch failed (see nvfp4_last_hip_error) */
+#define NVFP4_ESIZE (-6)        /* a caller buffer is smaller than required */
+
+/* Output element types. */
+#define NVFP4_OUT_F32 0
+#define NVFP4_OUT_BF16 1
+
+/* Epilogues of gemm_w4a4. */
+#define NVFP4_EPI_NONE 0
+#define NVFP4_EPI_SILU_MUL 1 /* out[:, j] = silu(y[:, j]) * y[:, j + n/2], j < n/2 */
+
+/* Per-segment epilogues of gemm_w4a4_fused_segments. */
+#define NVFP4_SEG_NONE 0
+#define NVFP4_SEG_SIGMOID 1   /* write strength: 1 / (1 + exp(-y)) */
+#define NVFP4_SEG_GDN_DECAY 2 /* decay: -exp(a_log[h]) * softplus(y + dt_bias[h]), h = column in segment */
+
+#define NVFP4_MAX_SEGMENTS 16
+
+/*
+ * nvfp4_quantize -- on-the-fly activation quantizer (the "A4" of W4A4;
+ * bayesiansapien page, TL;DR) with NVFP4 16-element block scaling
+ * (bayesiansapien page, mechanism study, first item).
+ *
+ *   x        bf16 [rows, cols], row stride ld_x elements (ld_x >= cols,
+ *            ld_x % 8 == 0 so rows are 16-byte aligned).
+ *   rows     >= 0; rows == 0 enqueues nothing (and leaves *global_scale).
+ *   cols     > 0, cols % 16 == 0.
+ *   global_scale  one device float.  dynamic_global != 0: the call writes
+ *            g = 2688 / max|x| (1 if x is all zero) there, on the device.
+ *            dynamic_global == 0: the call reads a calibrated g from there.
+ *   codes    out, uint8 [rows, cols/2], contiguous; low nibble = even column.
+ *            With dynamic_global, codes is also used as scratch for the
+ *            partial maxima before it is overwritten.
+ *   scales   out, E4M3 bytes [rows, cols/16], contiguous.
+ */
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                   float* global_scale, int dynamic_global,
+                   uint8_t* codes, uint8_t* scales, nvfp4_stream_t stream);
+
+/*
+ * nvfp4_packed_weight_bytes -- bytes of the opaque packed weight buffer for
+ * an [n, k] weight (k % 16 == 0); 0 for invalid sizes.  It is the NVFP4
+ * storage (k/2 + k/16 bytes per row, i.e. 4.5 bits per weight) of the weight
+ * padded to whole 32-row x 64-column tiles.
+ */
+size_t nvfp4_packed_weight_bytes(int64_t n, int64_t k);
+
+/*
+ * nvfp4_pack_weights -- offline weight quantizer/packer (the "W4" of W4A4;
+ * bayesiansapien page, TL;DR), with one global scale per module for fused
+ * weights (bayesiansapien page, "Two practical repairs").
+ *
+ *   w            bf16 [n, k], nn.Linear layout (row = output feature),
+ *                contiguous, k % 16 == 0, n >= 1.
+ *   num_segments 1..NVFP4_MAX_SEGMENTS; segment s is rows
+ *                [seg_offsets[s], seg_offsets[s+1]).
+ *   seg_offsets  host, num_segments+1 int64, 0 = first < ... < last = n.
+ *   seg_global   device float [num_segments]: written (2688/amax of the
+ *                segment) when dynamic_global != 0, else read (calibrated).
+ *   packed       out, opaque, nvfp4_packed_weight_bytes(n, k) bytes;
+ *                padding rows/columns hold zero codes and zero scales.
+ */
+int nvfp4_pack_weights(const uint16_t* w, int64_t n, int64_t k,
+                       int num_segments, const int64_t* seg_offsets,
+                       float* seg_global, int dynamic_global,
+                       void* packed, size_t packed_bytes, nvfp4_stream_t stream);
+
+/*
+ * nvfp4_unpack_weights_linear -- documented inverse of the packed layout:
+ * writes linear codes [n, k/2] and scales [n, k/16] (the layout
+ * nvfp4_quantize produces) so packed weights can be checked byte by byte.
+ */
+int nvfp4_unpack_weights_linear(const void* packed, int64_t n, int64_t k,
+                                uint8_t* codes, uint8_t* scales, nvfp4_stream_t stream);
+
+/*
+ * gemm_w4a4 -- block-scaled FP4 x FP4 GEMM with FP32 accumulation, the W4A4
+ * linear layer (bayesiansapien page, TL;DR; Figure node "Minima: NVFP4 W4A4
+ * all 496 linear layers"):
+ *     y[i][j] = alpha * sum_k a[i][k] * w[j][k],  alpha = 1 / (*a_global * *w_global)
+ * with a, w the dequantised NVFP4 elements (global scale not folded in).
+ *
+ *   a_codes, a_scales  the activation as written by nvfp4_quantize for an
+ *                      [m, k] tensor (contiguous).
+ *   a_global, w_global device floats (encode-form global scales).
+ *   m >= 0 (0 enqueues nothing), n >= 1, k >= 32, k % 32 == 0.
+ *   w_packed           from nvfp4_pack_weights with the same n, k.  A
+ *                      weight packed with several segments is treated as one
+ *                      module with scale *w_global (use the fused-segment
+ *                      entry point to apply each module's own scale).
+ *   out                [m, n] (epilogue NONE) or [m, n/2] (SILU_MUL), row
+ *                      stride ld_out elements, element type out_dtype
+ *                      (out aligned to its element size).
+ *   epilogue           NONE, or SILU_MUL: requires n % 64 == 0 and computes
+ *                      out[:, j] = silu(y[:, j]) * y[:, j + n/2].
+ * m <= 64 runs the weight-streaming decode kernel, larger m the tiled
+ * prefill kernel; both give results within 1e-5 * sum_k |a*w| * alpha.
+ */
+int gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t m,
+              const void* w_packed, const float* w_global, int64_t n, int64_t k,
+              void* out, int out_dtype, int64_t ld_out, int epilogue, nvfp4_stream_t stream);
+
+/*
+ * gemm_w4a4_fused_segments -- one GEMM over a fused weight whose column
+ * segments are separately calibrated modules: the global-scale-mismatch
+ * repair of the bayesiansapien page ("Two practical repairs") and aimodeling
+ * page ("What engineers should actually take away").  Output column j of
+ * segment s gets alpha_s = 1 / (*a_global * seg_w_global[s]), then the
+ * segment's epilogue (the Gated DeltaNet gate parameterisations of the
+ * bayesiansapien page, mechanism study, second item).
+ *
+ *   A, m, k, w_packed, n, out, out_dtype, ld_out as for gemm_w4a4.
+ *   num_segments  1..NVFP4_MAX_SEGMENTS; seg_offsets host int64
+ *                 [num_segments+1], 0 = first < ... < last = n.
+ *   seg_w_global  device float [num_segments].
+ *   seg_epilogue  host int [num_segments]: NVFP4_SEG_NONE / SIGMOID / GDN_DECAY.
+ *   a_log, dt_bias device float, one per column of the (at most one)
+ *                 GDN_DECAY segment; may be null if no segment uses it.
+ */
+int gemm_w4a4_fused_segments(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                             int64_t m, const void* w_packed, int64_t n, int64_t k,
+                             int num_segments, const int64_t* seg_offsets, const float* seg_w_global,
+                             const int* seg_epilogue, const float* a_log, const float* dt_bias,
+                             void* out, int out_dtype, int64_t ld_out, nvfp4_stream_t stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* nvfp4_status_string(int status);
+
+/* The HIP error code of the last NVFP4_EHIP returned on this thread (0 if none). */
+int nvfp4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

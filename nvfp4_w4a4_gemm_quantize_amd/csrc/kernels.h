@@ -1,0 +1,43 @@
+// Internal launcher interface between the C ABI layer and the HIP kernels.
+// Launchers enqueue on the given stream and return the launch status; all
+// argument validation happens before they are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kMaxSegments = 16;
+
+// Row (packer) or column (GEMM) segments of a fused weight, passed by value
+// as a kernel argument.
+struct SegmentTable {
+  int64_t off[kMaxSegments + 1];
+  int num;
+};
+
+// Per-output-column epilogue description for the GEMM kernels.
+struct EpilogueArgs {
+  SegmentTable segs;            // column segments (num == 1 for a plain GEMM)
+  int seg_epi[kMaxSegments];    // NVFP4_SEG_* per segment
+  const float* seg_w_global;    // device [num] weight global scales
+  const float* a_global;        // device scalar activation global scale
+  const float* a_log;           // device, per column of the decay segment
+  const float* dt_bias;         // device, per column of the decay segment
+  int silu_mul;                 // 1: out[:, j] = silu(y[:, j]) * y[:, j + n/2]
+  int out_bf16;                 // 1: bf16 output, 0: fp32
+  int64_t ld_out;
+};
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* g,
+                           bool dynamic, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const SegmentTable& segs, float* seg_g,
+                       bool dynamic, uint8_t* packed, hipStream_t st);
+hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                         hipStream_t st);
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
+                       int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);
+
+}  // namespace nvfp4

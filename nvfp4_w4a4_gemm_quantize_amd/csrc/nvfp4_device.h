@@ -1,0 +1,143 @@
+// Device helpers shared by the gfx950 NVFP4 kernels: bf16 access, E4M3
+// encode/decode, the 16-element block quantizer and the exact in-register
+// NVFP4 -> f16 dequantiser that feeds the f16 MFMA.
+//
+// Format (NVFP4; one E4M3 scale per 16 elements -- bayesiansapien page, "The
+// four-part mechanism study", first item): E2M1 codes, low nibble = even
+// element; E4M3FN scale bytes; FP32 global scale in encode form.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr float kGlobalNumerator = 2688.0f;  // E2M1 max (6) * E4M3 max (448)
+constexpr float kE4M3Max = 448.0f;
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xFFFF0000u); }
+
+// max over |bf16| of 8 packed values, as the 15-bit magnitude pattern (monotone in |x|).
+__device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
+  uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
+  uint32_t m0 = max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16));
+  uint32_t m1 = max(max(c & 0xFFFFu, c >> 16), max(d & 0xFFFFu, d >> 16));
+  return max(m0, m1);
+}
+
+// --------------------------------------------------------------- E4M3 ----
+// Round a magnitude u in [0, 448] to the nearest E4M3FN byte, ties to the even
+// mantissa.  Below 2^-6 the E4M3 grid is uniform with step 2^-9 (subnormals,
+// continuing into 2^-6 = code 8), so rounding is rint(u * 2^9); above, the
+// FP32 significand is rounded to 3 bits with the usual carry into the exponent.
+__device__ __forceinline__ uint32_t e4m3_encode_rne(float u) {
+  uint32_t b = __float_as_uint(u);
+  if (b < 0x3C800000u) {                 // u < 2^-6
+    return (uint32_t)__builtin_rintf(u * 512.0f);
+  }
+  uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return (r >> 20) - (120u << 3);        // rebias exponent 127 -> 7
+}
+
+// Exact value of an E4M3FN byte in [0, 0x7E].
+__device__ __forceinline__ float e4m3_decode(uint32_t s) {
+  uint32_t e = s >> 3, m = s & 7u;
+  if (e == 0) return (float)m * 0x1p-9f;
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------- block quantizer ----
+// Quantise 16 bf16 values (two uint4) with global scale g.  Writes 8 code
+// bytes (low nibble = even element) and returns the E4M3 scale byte.
+//   u = min((m/6)*g, 448); S = E4M3 RNE(u); S == 0 -> codes 0;
+//   r = g / value(S); code_i = fp4_rne_sat(x_i * r) with the sign of x_i.
+// Every step is one IEEE FP32 operation (correctly rounded division; the
+// hardware FP32 -> E2M1 conversion rounds to nearest even, saturates at 6
+// and keeps the sign, with a unit scale).
+__device__ __forceinline__ uint32_t quantize_block16(uint4 lo, uint4 hi, float g, uint2* codes_out) {
+  uint32_t mbits = max(absmax_bits8(lo), absmax_bits8(hi));
+  float m = __uint_as_float(mbits << 16);
+  float t = m / 6.0f;
+  float u = fminf(t * g, kE4M3Max);
+  uint32_t S = e4m3_encode_rne(u);
+  uint2 c = make_uint2(0u, 0u);
+  if (S != 0) {
+    float r = g / e4m3_decode(S);
+    uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
+    uint32_t v[4] = {hi.x, hi.y, hi.z, hi.w};
+    uint32_t c0 = 0, c1 = 0;
+    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[0]) * r, bf16_hi(w[0]) * r, 1.0f, 0);
+    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[1]) * r, bf16_hi(w[1]) * r, 1.0f, 1);
+    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[2]) * r, bf16_hi(w[2]) * r, 1.0f, 2);
+    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[3]) * r, bf16_hi(w[3]) * r, 1.0f, 3);
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[0]) * r, bf16_hi(v[0]) * r, 1.0f, 0);
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[1]) * r, bf16_hi(v[1]) * r, 1.0f, 1);
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[2]) * r, bf16_hi(v[2]) * r, 1.0f, 2);
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[3]) * r, bf16_hi(v[3]) * r, 1.0f, 3);
+    c = make_uint2(c0, c1);
+  }
+  *codes_out = c;
+  return S;
+}
+
+// --------------------------------------------------------- dequantiser ----
+// E4M3 byte s as an f16 bit pattern: (s << 7) read as f16 is value(s) * 2^-8
+// for every s (exponent and mantissa fields line up; E4M3 subnormals become
+// f16 subnormals).  Two copies packed for v_pk_mul_f16.
+__device__ __forceinline__ half2_t scale_pair_f16(uint32_t s) {
+  uint32_t b = (s << 7) | (s << 23);
+  return __builtin_bit_cast(half2_t, b);
+}
+
+// 8 E2M1 codes (one dword, low nibble first) times one E4M3 scale -> 8 exact
+// f16 values.  The hardware FP4 -> f16 conversion applies only the exponent
+// of its scale operand, so it is given 2^8 and the scale's 2^-8-shifted f16
+// (mantissa included) is applied with v_pk_mul_f16; every product e2m1 * s
+// has at most 6 significant bits and lies in [2^-10, 2688], so it is exact.
+__device__ __forceinline__ half8_t dequant8(uint32_t codes, half2_t sc) {
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * sc;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * sc;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * sc;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * sc;
+  half8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ floatx16 mfma32x32x16(half8_t a, half8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------- outputs ----
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------- wave reductions ----
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// --------------------------------------------------- packed weight layout ----
+// Weights are stored in tiles of 32 rows (output features) x 64 columns (K).
+// Tile (nt, kt) holds 1024 code bytes in MFMA lane order -- lane l = c + 32*h
+// owns the 16 bytes of row c, columns 32h..32h+31 -- followed, in a separate
+// region after all codes, by 128 scale bytes: row c's four block scales at
+// c*4..c*4+3.  Tiles are ordered nt-major (a row of tiles along K is
+// contiguous), so a wave streams one 32-row slab with fully coalesced 16-byte
+// loads.
+constexpr int kTileN = 32;
+constexpr int kTileK = 64;
+constexpr int kTileCodeBytes = kTileN * kTileK / 2;   // 1024
+constexpr int kTileScaleBytes = kTileN * kTileK / 16; // 128
+
+}  // namespace nvfp4

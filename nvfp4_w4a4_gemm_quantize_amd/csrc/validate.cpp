@@ -1,0 +1,70 @@
+// Host-side argument validation of the C ABI (no HIP dependency).
+#include "validate.h"
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const void* global_scale,
+                      const void* codes, const void* scales) {
+  if (rows < 0 || cols <= 0) return NVFP4_ESHAPE;
+  if (cols % 16 != 0 || ld_x < cols) return NVFP4_ESHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !global_scale || !codes || !scales) return NVFP4_EINVAL;
+  if (ld_x % 8 != 0 || !aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(global_scale) & 3u))
+    return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+size_t packed_weight_bytes(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0 || k % 16 != 0) return 0;
+  const int64_t np = (n + 31) / 32 * 32, kp = (k + 63) / 64 * 64;
+  return (size_t)(np * kp / 2 + np * kp / 16);
+}
+
+int validate_segments(int num_segments, const int64_t* seg_offsets, int64_t extent) {
+  if (num_segments < 1 || num_segments > NVFP4_MAX_SEGMENTS) return NVFP4_EINVAL;
+  if (!seg_offsets) return NVFP4_EINVAL;
+  if (seg_offsets[0] != 0 || seg_offsets[num_segments] != extent) return NVFP4_ESHAPE;
+  for (int s = 0; s < num_segments; ++s)
+    if (seg_offsets[s] >= seg_offsets[s + 1]) return NVFP4_ESHAPE;
+  return NVFP4_OK;
+}
+
+int validate_pack(const void* w, int64_t n, int64_t k, int num_segments, const int64_t* seg_offsets,
+                  const void* seg_global, const void* packed, size_t packed_bytes) {
+  if (n <= 0 || k <= 0 || k % 16 != 0) return NVFP4_ESHAPE;
+  int rc = validate_segments(num_segments, seg_offsets, n);
+  if (rc) return rc;
+  if (!w || !seg_global || !packed) return NVFP4_EINVAL;
+  if (!aligned16(w) || !aligned16(packed) || (reinterpret_cast<uintptr_t>(seg_global) & 3u)) return NVFP4_EALIGN;
+  if (packed_bytes < packed_weight_bytes(n, k)) return NVFP4_ESIZE;
+  return NVFP4_OK;
+}
+
+int validate_unpack(const void* packed, int64_t n, int64_t k, const void* codes, const void* scales) {
+  if (n <= 0 || k <= 0 || k % 16 != 0) return NVFP4_ESHAPE;
+  if (!packed || !codes || !scales) return NVFP4_EINVAL;
+  if (!aligned16(packed) || (reinterpret_cast<uintptr_t>(codes) & 7u)) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+int validate_gemm_common(const void* a_codes, const void* a_scales, const void* a_global, int64_t m,
+                         const void* w_packed, int64_t n, int64_t k, const void* out, int out_dtype,
+                         int64_t ld_out, int64_t out_cols) {
+  if (m < 0 || n <= 0 || k <= 0) return NVFP4_ESHAPE;
+  if (k % 32 != 0) return k % 16 == 0 ? NVFP4_EUNSUPPORTED : NVFP4_ESHAPE;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_EINVAL;
+  if (ld_out < out_cols) return NVFP4_ESHAPE;
+  if (m == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_global || !w_packed || !out) return NVFP4_EINVAL;
+  const uintptr_t elem = out_dtype == NVFP4_OUT_F32 ? 4u : 2u;
+  if (!aligned16(a_codes) || !aligned16(w_packed) || (reinterpret_cast<uintptr_t>(a_scales) & 3u) ||
+      (reinterpret_cast<uintptr_t>(out) & (elem - 1)))
+    return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+}  // namespace nvfp4

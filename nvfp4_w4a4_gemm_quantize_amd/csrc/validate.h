@@ -1,0 +1,20 @@
+// Host-side argument validation of the C ABI.  Pure C++ (no HIP headers), so
+// it can be compiled and exercised on a machine without a GPU.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+int validate_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const void* global_scale,
+                      const void* codes, const void* scales);
+size_t packed_weight_bytes(int64_t n, int64_t k);
+int validate_segments(int num_segments, const int64_t* seg_offsets, int64_t extent);
+int validate_pack(const void* w, int64_t n, int64_t k, int num_segments, const int64_t* seg_offsets,
+                  const void* seg_global, const void* packed, size_t packed_bytes);
+int validate_unpack(const void* packed, int64_t n, int64_t k, const void* codes, const void* scales);
+int validate_gemm_common(const void* a_codes, const void* a_scales, const void* a_global, int64_t m,
+                         const void* w_packed, int64_t n, int64_t k, const void* out, int out_dtype,
+                         int64_t ld_out, int64_t out_cols);
+
+}  // namespace nvfp4

@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/nvfp4.h declares, and rejects invalid arguments with the documented
+status codes before touching the device (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_w4a4_gemm_quantize_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
+
+OK, EINVAL, ESHAPE, EALIGN, EUNSUPPORTED, EHIP, ESIZE = 0, -1, -2, -3, -4, -5, -6
+A16 = 0x10000          # a 16-byte-aligned fake device address (never dereferenced)
+MIS = 0x10004          # a misaligned one
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    # These calls pass fake device addresses that validation must reject; they
+    # are meant for a host without a GPU, where no launch could ever happen.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("validation tests with fake device pointers run on GPU-less hosts only")
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libnvfp4.so is not built; run __graft_entry__.build() first")
+    return binding.load()
+
+
+def test_header_declares_the_four_entry_points_and_helpers():
+    fns = declared_functions()
+    for name in ("nvfp4_quantize", "nvfp4_pack_weights", "gemm_w4a4", "gemm_w4a4_fused_segments",
+                 "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights_linear", "nvfp4_status_string",
+                 "nvfp4_last_hip_error"):
+        assert name in fns
+    assert set(fns) == set(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (OK, EINVAL, ESHAPE, EALIGN, EUNSUPPORTED, EHIP, ESIZE):
+        assert lib.nvfp4_status_string(code)
+    assert lib.nvfp4_status_string(123) == b"unknown status"
+    assert lib.nvfp4_last_hip_error() == 0
+
+
+def test_packed_weight_bytes(lib):
+    f = lib.nvfp4_packed_weight_bytes
+    assert f(17408, 5120) == 17408 * 5120 * 9 // 16          # 4.5 bits per weight, no padding
+    assert f(16480, 5120) == 16480 * 5120 * 9 // 16
+    assert f(100, 80) == 128 * 128 * 9 // 16                 # padded to 32 x 64 tiles
+    assert f(0, 64) == 0 and f(64, 0) == 0 and f(64, 24) == 0 and f(-1, 64) == 0
+
+
+def q(lib, x=A16, rows=4, cols=64, ld=64, g=A16, dyn=1, codes=A16, scales=A16):
+    return lib.nvfp4_quantize(x, rows, cols, ld, g, dyn, codes, scales, None)
+
+
+def test_quantize_validation(lib):
+    assert q(lib, cols=24, ld=24) == ESHAPE          # cols % 16
+    assert q(lib, cols=0, ld=0) == ESHAPE
+    assert q(lib, rows=-1) == ESHAPE
+    assert q(lib, ld=32) == ESHAPE                   # ld < cols
+    assert q(lib, x=None) == EINVAL
+    assert q(lib, g=None) == EINVAL
+    assert q(lib, codes=None) == EINVAL
+    assert q(lib, scales=None) == EINVAL
+    assert q(lib, x=MIS) == EALIGN
+    assert q(lib, ld=68) == EALIGN                   # rows not 16-byte aligned
+    assert q(lib, codes=MIS) == EALIGN
+    assert q(lib, rows=0, x=None, codes=None) == OK  # empty input: nothing to do
+
+
+def pk(lib, w=A16, n=64, k=128, nseg=1, offs=(0, 64), g=A16, dyn=1, packed=A16, nbytes=None):
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    if nbytes is None:
+        nbytes = lib.nvfp4_packed_weight_bytes(n, k)
+    return lib.nvfp4_pack_weights(w, n, k, nseg, arr, g, dyn, packed, nbytes, None)
+
+
+def test_pack_validation(lib):
+    assert pk(lib, k=24) == ESHAPE
+    assert pk(lib, n=0, offs=(0, 0)) == ESHAPE
+    assert pk(lib, nseg=0) == EINVAL
+    assert pk(lib, nseg=17, offs=tuple(range(0, 18))) == EINVAL
+    assert pk(lib, nseg=2, offs=(0, 40, 40)) == ESHAPE           # last != n
+    assert pk(lib, nseg=2, offs=(0, 70, 64)) == ESHAPE           # not rising
+    assert pk(lib, nseg=2, offs=(1, 30, 64)) == ESHAPE           # first != 0
+    assert pk(lib, w=None) == EINVAL
+    assert pk(lib, packed=None) == EINVAL
+    assert pk(lib, g=None) == EINVAL
+    assert pk(lib, w=MIS) == EALIGN
+    assert pk(lib, nbytes=100) == ESIZE
+    assert lib.nvfp4_pack_weights(A16, 64, 128, 1, None, A16, 1, A16, 9000, None) == EINVAL
+
+
+def gm(lib, ac=A16, asc=A16, ag=A16, m=64, w=A16, wg=A16, n=128, k=128, out=A16, dt=1, ld=128, epi=0):
+    return lib.gemm_w4a4(ac, asc, ag, m, w, wg, n, k, out, dt, ld, epi, None)
+
+
+def test_gemm_validation(lib):
+    assert gm(lib, k=48) == EUNSUPPORTED       # a valid NVFP4 K (16 | K) this build does not run
+    assert gm(lib, k=40) == ESHAPE
+    assert gm(lib, n=0) == ESHAPE
+    assert gm(lib, m=-3) == ESHAPE
+    assert gm(lib, dt=7) == EINVAL
+    assert gm(lib, epi=5) == EINVAL
+    assert gm(lib, epi=1, n=96) == ESHAPE      # SiLU*mul needs n % 64
+    assert gm(lib, ld=100) == ESHAPE           # ld_out < n
+    assert gm(lib, epi=1, ld=60) == ESHAPE    # SiLU*mul output has n/2 = 64 columns
+    assert gm(lib, out=0x10002, dt=0) == EALIGN   # fp32 output must be 4-byte aligned
+    assert gm(lib, ac=None) == EINVAL
+    assert gm(lib, wg=None) == EINVAL
+    assert gm(lib, out=None) == EINVAL
+    assert gm(lib, ac=MIS) == EALIGN
+    assert gm(lib, w=MIS) == EALIGN
+    assert gm(lib, m=0, ac=None, out=None) == OK
+
+
+def fs(lib, m=64, n=128, k=128, nseg=2, offs=(0, 64, 128), epis=(0, 1), alog=A16, dtb=A16, sg=A16, ld=128):
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    ep = (ctypes.c_int * len(epis))(*epis)
+    return lib.gemm_w4a4_fused_segments(A16, A16, A16, m, A16, n, k, nseg, arr, sg, ep, alog, dtb, A16, 1, ld, None)
+
+
+def test_fused_segments_validation(lib):
+    assert fs(lib, offs=(0, 64, 120)) == ESHAPE
+    assert fs(lib, epis=(0, 9)) == EINVAL
+    assert fs(lib, epis=(2, 2)) == EUNSUPPORTED          # at most one decay segment
+    assert fs(lib, epis=(0, 2), alog=None) == EINVAL
+    assert fs(lib, sg=None) == EINVAL
+    assert fs(lib, nseg=0, offs=(0,), epis=(0,)) == EINVAL
+    assert fs(lib, k=80) == EUNSUPPORTED
+    assert fs(lib, m=0, sg=None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    with pytest.raises(binding.NVFP4Error):
+        binding.nvfp4_quantize(x)

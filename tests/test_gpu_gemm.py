@@ -1,0 +1,290 @@
+"""GPU parity of the W4A4 GEMMs against the fp64 oracle.
+
+Inputs come from the seeded generators and are quantised by the oracle for
+the expected side; the GPU side runs the whole HIP path (quantizer, packer,
+GEMM).  Acceptance per element: |y_gpu - y| <= 1e-5 * sum_k |a_k w_k| * alpha
+(+ bf16 output rounding), bit-exact where the GEMM is an exact small-integer
+product, and Lipschitz-propagated bounds through the epilogues.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_w4a4_gemm_quantize_amd import inputs
+from oracle import formats as F
+from tests.parity import (OE, OG, OQ, check_gemm, dev_bf16, f32, gpu_out_f64, host, assert_within,
+                          oracle_gemm_rows, oracle_quantize_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_prepare(lib, a_bits, w_bits, offs=None, a_g=None, w_g=None):
+    """Quantise A and pack W on the GPU (dynamic scales unless given)."""
+    a = dev_bf16(a_bits)
+    ac, asc, ag = lib.nvfp4_quantize(a, None if a_g is None else f32([a_g]), dynamic=a_g is None)
+    packed, wg = lib.nvfp4_pack_weights(dev_bf16(w_bits), offs, None if w_g is None else f32(w_g),
+                                        dynamic=w_g is None)
+    return ac, asc, ag, packed, wg
+
+
+def oracle_prepare(a_bits, w_bits, offs=None, a_g=None, w_g=None, rows=None):
+    ca, sa, ga = OQ.quantize(a_bits, a_g)
+    n = w_bits.shape[0]
+    offs = [0, n] if offs is None else list(offs)
+    if w_g is None:
+        gs = np.array([OQ.dynamic_global_scale(w_bits[offs[i]:offs[i + 1]]) for i in range(len(offs) - 1)],
+                      dtype=np.float32)
+    else:
+        gs = np.asarray(w_g, dtype=np.float32)
+    cw = np.empty((n, w_bits.shape[1] // 2), np.uint8)
+    sw = np.empty((n, w_bits.shape[1] // 16), np.uint8)
+    for i in range(len(offs) - 1):
+        cw[offs[i]:offs[i + 1]], sw[offs[i]:offs[i + 1]] = oracle_quantize_rows(w_bits[offs[i]:offs[i + 1]], gs[i])
+    if rows is not None:
+        ca, sa = ca[rows], sa[rows]
+    return ca, sa, ga, cw, sw, gs, OG.column_global(n, offs, gs)
+
+
+# ------------------------------------------------------------ exactness ----
+def test_unit_scales_give_the_exact_integer_product(gpu_lib):
+    """Oracle pin P8 on the GPU: scale 1.0, g = 1, K = 128 -> exact fp32 result."""
+    rng = np.random.default_rng(80)
+    for (M, N) in [(16, 64), (100, 96), (1, 64)]:
+        K = 128
+        ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+        cw = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+        cw[:, ::16] = 7                                       # a +6 per block -> scale exactly 1.0
+        ca[:, ::16] = 15                                      # a -6 per block
+        a_bits = inputs.f32_to_bf16_bits(F.E2M1_TABLE[ca].astype(np.float32))
+        w_bits = inputs.f32_to_bf16_bits(F.E2M1_TABLE[cw].astype(np.float32))
+        ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits, a_g=1.0, w_g=[1.0])
+        assert np.all(host(asc) == 0x38)
+        y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.float32)
+        ia = np.rint(2 * F.E2M1_TABLE[ca]).astype(np.int64)
+        iw = np.rint(2 * F.E2M1_TABLE[cw]).astype(np.int64)
+        np.testing.assert_array_equal(host(y).astype(np.float64) * 4, (ia @ iw.T).astype(np.float64))
+
+
+# ------------------------------------------------------ full comparison ----
+@pytest.mark.parametrize("M,N,K,out", [
+    (16, 64, 128, "f32"),        # the tiny workload's shape
+    (300, 520, 320, "bf16"),     # several tiles, ragged M and N tails, 5 K tiles
+    (129, 100, 96, "f32"),       # N not a multiple of 32, K % 64 == 32
+    (65, 160, 64, "bf16"),       # just above the decode limit, a single K tile
+    (37, 96, 5120, "f32"),       # decode kernel, long K
+    (1, 33, 32, "f32"),          # smallest K
+    (512, 256, 1024, "bf16"),
+])
+def test_gemm_matches_oracle_everywhere(gpu_lib, M, N, K, out):
+    rng = np.random.default_rng(M * 1000003 + N * 101 + K)
+    a = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    a[:, rng.choice(K, max(1, K // 1000), replace=False)] *= 50
+    w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    a_bits, w_bits = inputs.f32_to_bf16_bits(a), inputs.f32_to_bf16_bits(w)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits)
+    y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K,
+                          out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    check_gemm(gpu_out_f64(y), yr, br, out == "bf16", "gemm %dx%dx%d" % (M, N, K))
+
+
+def test_tiny_workload(gpu_lib):
+    d = inputs.tiny()
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, d["A"], d["W"])
+    y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, 64, 128, out_dtype=torch.float32)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(d["A"], d["W"])
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    check_gemm(gpu_out_f64(y), yr, br, False, "tiny")
+
+
+# ---------------------------------------------------- full-size configs ----
+def sample_rows(M, count=24, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, M // 2, M - 1]
+    return np.unique(np.concatenate([fixed, rng.choice(M, count, replace=False)]))
+
+
+def test_linear_prefill_config(gpu_lib):
+    d = inputs.linear()
+    M, N, K = 2048, 5120, 5120
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, d["A"], d["W"])
+    y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.bfloat16)
+    rows = sample_rows(M)
+    got = gpu_out_f64(y[torch.as_tensor(rows, device="cuda")])
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(d["A"], d["W"], rows=rows)
+    yr, br = oracle_gemm_rows(ca, sa, ga, cw, sw, gcol)
+    check_gemm(got, yr, br, True, "linear prefill")
+
+
+@pytest.mark.parametrize("M", inputs.DECODE_M)
+def test_decode_config(gpu_lib, M):
+    d = inputs.decode(M)
+    N, K = 17408, 5120
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, d["A"], d["W"])
+    y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.bfloat16)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(d["A"], d["W"])
+    yr, br = oracle_gemm_rows(ca, sa, ga, cw, sw, gcol)
+    check_gemm(gpu_out_f64(y), yr, br, True, "decode M=%d" % M)
+
+
+def test_mlp_config_stages(gpu_lib):
+    """MLP block: (i) gate_up + SiLU*mul, (iii) down-projection on the oracle's
+    quantised h; and the whole GPU chain run end to end (reported by finiteness)."""
+    d = inputs.mlp()
+    M, K, N2, KD = 4096, 5120, 34816, 17408
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, d["A"], d["W_gate_up"])
+    h = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N2, K, out_dtype=torch.bfloat16, epilogue="silu_mul")
+    rows = sample_rows(M, 16)
+    got = gpu_out_f64(h[torch.as_tensor(rows, device="cuda")])
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(d["A"], d["W_gate_up"], rows=rows)
+    yr, br = oracle_gemm_rows(ca, sa, ga, cw, sw, gcol)
+    g_, u_ = yr[:, :KD], yr[:, KD:]
+    tg, tu = OG.GEMM_REL_TOL * br[:, :KD], OG.GEMM_REL_TOL * br[:, KD:]
+    assert_within(got, OE.silu_mul(g_, u_), OE.silu_mul_tolerance(g_, u_, tg, tu, True), "gate_up silu*mul")
+    # (iii) down-projection on the oracle's own h (bf16) for 96 rows (prefill path)
+    h_or = OG.f64_to_bf16_bits(OE.silu_mul(g_, u_))
+    h_rows = np.concatenate([h_or] * 6)[:96]
+    ac2, asc2, ag2, packed2, wg2 = gpu_prepare(gpu_lib, h_rows, d["W_down"])
+    y2 = gpu_lib.gemm_w4a4(ac2, asc2, ag2, packed2, wg2, 5120, KD, out_dtype=torch.bfloat16)
+    ca2, sa2, ga2, cw2, sw2, gs2, gcol2 = oracle_prepare(h_rows, d["W_down"])
+    yr2, br2 = oracle_gemm_rows(ca2, sa2, ga2, cw2, sw2, gcol2)
+    check_gemm(gpu_out_f64(y2), yr2, br2, True, "down K=17408")
+    # the GPU chain end to end
+    hq, hs, hg = gpu_lib.nvfp4_quantize(h)
+    y3 = gpu_lib.gemm_w4a4(hq, hs, hg, packed2, wg2, 5120, KD, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y3.float()).all()
+
+
+def gdn_reference(yr, br, offs, a_log, dt_bias):
+    """Oracle output of the fused in-projection and its per-element tolerance."""
+    ref = yr.copy()
+    tol = OG.tolerance(br, yr, True)
+    b0, b1, a0, a1 = offs[4], offs[5], offs[5], offs[6]
+    ref[:, b0:b1] = OE.sigmoid(yr[:, b0:b1])
+    tol[:, b0:b1] = OE.sigmoid_tolerance(yr[:, b0:b1], OG.GEMM_REL_TOL * br[:, b0:b1], True)
+    ref[:, a0:a1] = OE.gdn_decay(yr[:, a0:a1], a_log, dt_bias)
+    tol[:, a0:a1] = OE.gdn_decay_tolerance(yr[:, a0:a1], a_log, dt_bias, OG.GEMM_REL_TOL * br[:, a0:a1], True)
+    return ref, tol
+
+
+def test_gdn_inproj_config_with_per_module_scales(gpu_lib):
+    d = inputs.gdn_inproj()
+    M, K = 4096, 5120
+    offs = [int(v) for v in d["seg_offsets"]]
+    N = offs[-1]
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, d["A"], d["W"], offs)
+    epis = ["none", "none", "none", "none", "sigmoid", "gdn_decay"]
+    y = gpu_lib.gemm_w4a4_fused_segments(ac, asc, ag, packed, N, K, offs, wg, epis,
+                                         f32(d["A_log"]), f32(d["dt_bias"]), out_dtype=torch.bfloat16)
+    rows = sample_rows(M, 16)
+    got = gpu_out_f64(y[torch.as_tensor(rows, device="cuda")])
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(d["A"], d["W"], offs, rows=rows)
+    assert gs.max() / gs.min() > 2.0          # the modules really are calibrated differently
+    yr, br = oracle_gemm_rows(ca, sa, ga, cw, sw, gcol)
+    ref, tol = gdn_reference(yr, br, offs, d["A_log"], d["dt_bias"])
+    assert_within(got, ref, tol, "gdn in-proj")
+
+
+def test_single_alpha_negative_control(gpu_lib):
+    """One alpha for the fused weight (the mis-scaling fused kernels do) is off per
+    segment by g_w[s] / g_w[0]; the per-segment entry point matches the oracle."""
+    d = inputs.gdn_inproj(M=256)
+    K = 5120
+    offs = [int(v) for v in d["seg_offsets"]]
+    N = offs[-1]
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, d["A"], d["W"], offs)
+    y_seg = gpu_lib.gemm_w4a4_fused_segments(ac, asc, ag, packed, N, K, offs, wg, None, out_dtype=torch.float32)
+    y_one = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg[:1], N, K, out_dtype=torch.float32)
+    gs = host(wg).astype(np.float64)
+    ys, yo = gpu_out_f64(y_seg), gpu_out_f64(y_one)
+    ca, sa, ga, cw, sw, ogs, gcol = oracle_prepare(d["A"], d["W"], offs)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    check_gemm(ys, yr, br, False, "per-segment alpha")
+    big = np.abs(yr) > 1e-3 * np.abs(yr).max()
+    for s in range(len(offs) - 1):
+        c = slice(offs[s], offs[s + 1])
+        ratio = yo[:, c][big[:, c]] / ys[:, c][big[:, c]]
+        np.testing.assert_allclose(ratio, gs[s] / gs[0], rtol=1e-5)
+        if abs(gs[s] / gs[0] - 1) > 0.01:
+            assert not np.all(np.abs(yo[:, c] - yr[:, c]) <= OG.tolerance(br[:, c], yr[:, c], False))
+
+
+@pytest.mark.parametrize("M", [1, 48, 200])
+def test_fused_segments_small(gpu_lib, M):
+    """Fused segments on small shapes, whole output compared, both kernels."""
+    rng = np.random.default_rng(M)
+    K = 256
+    widths = [64, 32, 48, 8, 40]
+    offs = list(np.cumsum([0] + widths))
+    N = offs[-1]
+    f = [1.0, 8.0, 0.5, 3.0, 2.0]
+    w = np.concatenate([rng.standard_normal((n, K)) * fs / 16 for n, fs in zip(widths, f)]).astype(np.float32)
+    a = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    a_bits, w_bits = inputs.f32_to_bf16_bits(a), inputs.f32_to_bf16_bits(w)
+    a_log = (rng.standard_normal(40) * 0.5).astype(np.float32)
+    dt = (rng.standard_normal(40) * 0.5).astype(np.float32)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits, offs)
+    epis = ["none", "sigmoid", "none", "sigmoid", "gdn_decay"]
+    y = gpu_lib.gemm_w4a4_fused_segments(ac, asc, ag, packed, N, K, offs, wg, epis, f32(a_log), f32(dt),
+                                         out_dtype=torch.bfloat16)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits, offs)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    ref = yr.copy()
+    tol = OG.tolerance(br, yr, True)
+    for s, e in enumerate(epis):
+        c = slice(offs[s], offs[s + 1])
+        t = OG.GEMM_REL_TOL * br[:, c]
+        if e == "sigmoid":
+            ref[:, c], tol[:, c] = OE.sigmoid(yr[:, c]), OE.sigmoid_tolerance(yr[:, c], t, True)
+        elif e == "gdn_decay":
+            ref[:, c] = OE.gdn_decay(yr[:, c], a_log, dt)
+            tol[:, c] = OE.gdn_decay_tolerance(yr[:, c], a_log, dt, t, True)
+    assert_within(gpu_out_f64(y), ref, tol, "fused segments M=%d" % M)
+
+
+@pytest.mark.parametrize("M", [1, 40, 130])
+def test_silu_mul_small(gpu_lib, M):
+    rng = np.random.default_rng(100 + M)
+    K, N = 192, 256
+    a = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    w = (rng.standard_normal((N, K)) / 8).astype(np.float32)
+    a_bits, w_bits = inputs.f32_to_bf16_bits(a), inputs.f32_to_bf16_bits(w)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits)
+    h = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.float32, epilogue="silu_mul")
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    g_, u_ = yr[:, :N // 2], yr[:, N // 2:]
+    tol = OE.silu_mul_tolerance(g_, u_, OG.GEMM_REL_TOL * br[:, :N // 2], OG.GEMM_REL_TOL * br[:, N // 2:], False)
+    assert_within(gpu_out_f64(h), OE.silu_mul(g_, u_), tol, "silu_mul M=%d" % M)
+
+
+# ------------------------------------------------- canaries, determinism ----
+@pytest.mark.parametrize("M", [7, 150])
+def test_output_canaries_and_run_to_run_identity(gpu_lib, M):
+    rng = np.random.default_rng(M)
+    K, N = 320, 200
+    a_bits = inputs.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w_bits = inputs.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits)
+    big = torch.full((M + 5, 264), -7.0, dtype=torch.float32, device="cuda")
+    view = big[:M, :N]
+    gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.float32, out=view)
+    first = host(big).copy()
+    assert np.all(first[:, N:] == -7.0) and np.all(first[M:, :] == -7.0)
+    gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.float32, out=view)
+    np.testing.assert_array_equal(host(big), first)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    check_gemm(first[:M, :N].astype(np.float64), yr, br, False, "strided out")
+
+
+def test_empty_m_is_a_no_op(gpu_lib):
+    rng = np.random.default_rng(3)
+    w_bits = inputs.f32_to_bf16_bits(rng.standard_normal((64, 128)).astype(np.float32))
+    packed, wg = gpu_lib.nvfp4_pack_weights(dev_bf16(w_bits))
+    ac = torch.empty((0, 64), dtype=torch.uint8, device="cuda")
+    asc = torch.empty((0, 8), dtype=torch.uint8, device="cuda")
+    y = gpu_lib.gemm_w4a4(ac, asc, f32([1.0]), packed, wg, 64, 128, out_dtype=torch.float32)
+    assert y.shape == (0, 64)
