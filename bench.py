@@ -1,0 +1,265 @@
+"""Benchmark of the NVFP4 W4A4 linear-layer hot path on one MI355X.
+
+One step = one pass of every kernel on the path over seeded synthetic inputs
+already resident in HBM:
+
+  prefill, M = 4096 tokens
+    quantize A (dynamic global scale)  -> fused GDN in-projection
+        (N = 16480 = q|k|v|z|b|a, K = 5120, per-module global scales,
+         sigmoid on b, -exp(A_log)*softplus(a + dt_bias) on a)
+    quantize A  -> MLP gate_up (N = 2 x 17408, K = 5120, SiLU*mul)
+        -> quantize h (dynamic) -> down (N = 5120, K = 17408)
+  decode, M = 1
+    quantize A -> GEMM (N = 17408, K = 5120) on one of 8 rotating copies of
+    the packed weight (8 x 50.1 MB > the 256 MB Infinity Cache)
+
+value = algorithmic GEMM FLOP (2MNK) of the prefill part / its wall time
+(quantizers and epilogues included), in TFLOP/s.  The decode part is
+reported as weight GB/s (packed weight bytes / GEMM time).  Kernel durations
+for the roofline are taken with HIP events on the stream the kernels run on.
+Weight packing is offline (done once, outside the timed region).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 NVFP4 GEMM TFLOP/s at M=4096 + weight GB/s at M=1; % of MI355X peak"
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense f16/bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0     # dense FP4 MFMA (context only: NVFP4's E4M3 scales do not fit it)
+PEAK_HBM_GBPS = 8000.0
+DECODE_COPIES = 8
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    return p.parse_args()
+
+
+def dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def setup(torch, B):
+    from nvfp4_w4a4_gemm_quantize_amd import inputs
+    t0 = time.time()
+    gdn = inputs.gdn_inproj()
+    mlp = inputs.mlp()
+    dec = inputs.decode(1)
+    S = {}
+    S["gdn_A"] = dev_bf16(torch, gdn["A"])
+    S["gdn_offs"] = [int(v) for v in gdn["seg_offsets"]]
+    S["gdn_packed"], S["gdn_g"] = B.nvfp4_pack_weights(dev_bf16(torch, gdn["W"]), S["gdn_offs"])
+    S["A_log"] = torch.tensor(gdn["A_log"], device="cuda")
+    S["dt_bias"] = torch.tensor(gdn["dt_bias"], device="cuda")
+    S["mlp_A"] = dev_bf16(torch, mlp["A"])
+    S["gu_packed"], S["gu_g"] = B.nvfp4_pack_weights(dev_bf16(torch, mlp["W_gate_up"]))
+    S["dn_packed"], S["dn_g"] = B.nvfp4_pack_weights(dev_bf16(torch, mlp["W_down"]))
+    S["dec_A"] = dev_bf16(torch, dec["A"])
+    p, g = B.nvfp4_pack_weights(dev_bf16(torch, dec["W"]))
+    S["dec_packed"] = [p] + [p.clone() for _ in range(DECODE_COPIES - 1)]
+    S["dec_g"] = g
+    M, K = 4096, 5120
+    # preallocated outputs and quantizer buffers
+    S["qa_codes"] = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    S["qa_scales"] = torch.empty((M, K // 16), dtype=torch.uint8, device="cuda")
+    S["qa_g"] = torch.empty(1, dtype=torch.float32, device="cuda")
+    S["qh_codes"] = torch.empty((M, 17408 // 2), dtype=torch.uint8, device="cuda")
+    S["qh_scales"] = torch.empty((M, 17408 // 16), dtype=torch.uint8, device="cuda")
+    S["qh_g"] = torch.empty(1, dtype=torch.float32, device="cuda")
+    S["gdn_out"] = torch.empty((M, 16480), dtype=torch.bfloat16, device="cuda")
+    S["h"] = torch.empty((M, 17408), dtype=torch.bfloat16, device="cuda")
+    S["mlp_out"] = torch.empty((M, 5120), dtype=torch.bfloat16, device="cuda")
+    S["qd_codes"] = torch.empty((1, K // 2), dtype=torch.uint8, device="cuda")
+    S["qd_scales"] = torch.empty((1, K // 16), dtype=torch.uint8, device="cuda")
+    S["qd_g"] = torch.empty(1, dtype=torch.float32, device="cuda")
+    S["dec_out"] = torch.empty((1, 17408), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    S["setup_s"] = time.time() - t0
+    return S
+
+
+FLOP = {
+    "gdn": 2 * 4096 * 16480 * 5120,
+    "gate_up": 2 * 4096 * 34816 * 5120,
+    "down": 2 * 4096 * 5120 * 17408,
+    "decode": 2 * 1 * 17408 * 5120,
+}
+DECODE_W_BYTES = 17408 * 5120 * 9 // 16          # packed codes + scales: 50,135,040
+DECODE_BYTES = DECODE_W_BYTES + 5120 * 9 // 16 + 17408 * 2
+
+
+def step(torch, B, S, it, ev):
+    """One pass; ev: dict name -> (start, end) events recorded around each kernel group."""
+    rec = (lambda name, i: ev[name][i].record()) if ev is not None else (lambda name, i: None)
+    rec("prefill", 0)
+    B.nvfp4_quantize(S["gdn_A"], S["qa_g"], True, S["qa_codes"], S["qa_scales"])
+    rec("gdn", 0)
+    B.gemm_w4a4_fused_segments(S["qa_codes"], S["qa_scales"], S["qa_g"], S["gdn_packed"], 16480, 5120,
+                               S["gdn_offs"], S["gdn_g"], ["none", "none", "none", "none", "sigmoid", "gdn_decay"],
+                               S["A_log"], S["dt_bias"], out=S["gdn_out"])
+    rec("gdn", 1)
+    B.nvfp4_quantize(S["mlp_A"], S["qa_g"], True, S["qa_codes"], S["qa_scales"])
+    rec("gate_up", 0)
+    B.gemm_w4a4(S["qa_codes"], S["qa_scales"], S["qa_g"], S["gu_packed"], S["gu_g"], 34816, 5120,
+                epilogue="silu_mul", out=S["h"])
+    rec("gate_up", 1)
+    B.nvfp4_quantize(S["h"], S["qh_g"], True, S["qh_codes"], S["qh_scales"])
+    rec("down", 0)
+    B.gemm_w4a4(S["qh_codes"], S["qh_scales"], S["qh_g"], S["dn_packed"], S["dn_g"], 5120, 17408, out=S["mlp_out"])
+    rec("down", 1)
+    rec("prefill", 1)
+    rec("decode_all", 0)
+    B.nvfp4_quantize(S["dec_A"], S["qd_g"], True, S["qd_codes"], S["qd_scales"])
+    rec("decode", 0)
+    B.gemm_w4a4(S["qd_codes"], S["qd_scales"], S["qd_g"], S["dec_packed"][it % DECODE_COPIES], S["dec_g"],
+                17408, 5120, out=S["dec_out"])
+    rec("decode", 1)
+    rec("decode_all", 1)
+
+
+def decode_sweep(torch, B, S, iters=50):
+    """Weight GB/s of the decode GEMM at each M (rotating weight copies), after the timed region."""
+    from nvfp4_w4a4_gemm_quantize_amd import inputs
+    out = {}
+    for M in inputs.DECODE_M:
+        a = dev_bf16(torch, inputs.decode(M, weights=False)["A"])
+        qc, qs, qg = B.nvfp4_quantize(a)
+        y = torch.empty((M, 17408), dtype=torch.bfloat16, device="cuda")
+        for i in range(5):
+            B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(iters):
+            B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
+        e1.record()
+        q0.record()
+        for i in range(iters):
+            B.nvfp4_quantize(a, qg, True, qc, qs)
+            B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
+        q1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000 / iters
+        us_q = q0.elapsed_time(q1) * 1000 / iters
+        nbytes = DECODE_W_BYTES + M * (5120 * 9 // 16) + M * 17408 * 2
+        out["M%d" % M] = {"gemm_us": round(us, 2), "weight_GBps": round(DECODE_W_BYTES / us / 1e3, 1),
+                          "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 3),
+                          "quantize_plus_gemm_us": round(us_q, 2),
+                          "tflops": round(2 * M * 17408 * 5120 / us / 1e6, 2)}
+    return out
+
+
+def cpu_baseline(target_s):
+    """The CPU oracle on a row sample of the same prefill workload, scaled to TFLOP/s."""
+    from threadpoolctl import threadpool_limits
+    from nvfp4_w4a4_gemm_quantize_amd import inputs
+    from oracle import epilogue as OE
+    from oracle import gemm as OG
+    from oracle import quantize as OQ
+    cores = min(16, len(os.sched_getaffinity(0)))
+    gdn = inputs.gdn_inproj()
+    offs = [int(v) for v in gdn["seg_offsets"]]
+    with threadpool_limits(limits=cores):
+        cw, sw, gs = OQ.quantize_segments(gdn["W"], offs)          # offline weight pack: untimed
+        gcol = OG.column_global(offs[-1], offs, gs)
+        t0 = time.perf_counter()
+        g_a = OQ.dynamic_global_scale(gdn["A"])                    # per-tensor amax of the whole batch
+        flops, spent, rows_done, r0 = 0, time.perf_counter() - t0, 0, 0
+        rows = 16
+        while spent < target_s and r0 + rows <= 4096:
+            t0 = time.perf_counter()
+            ca, sa, ga = OQ.quantize(gdn["A"][r0:r0 + rows], g_a)
+            y, b = OG.gemm(ca, sa, ga, cw, sw, gcol)
+            OE.sigmoid(y[:, offs[4]:offs[5]])
+            OE.gdn_decay(y[:, offs[5]:offs[6]], gdn["A_log"], gdn["dt_bias"])
+            spent += time.perf_counter() - t0
+            flops += 2 * rows * offs[-1] * 5120
+            rows_done += rows
+            r0 += rows
+            rows = min(rows * 2, 256)
+    return {"value": round(flops / spent / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "fused GDN in-projection (N=16480, K=5120, 6 modules, sigmoid/decay epilogues) on the "
+                      "first %d of 4096 rows: numpy FP32 quantizer + fp64 dequant GEMM with the sum|a*w| bound; "
+                      "%.1f s" % (rows_done, spent)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: the library has no multi-GPU path and this build uses one GPU "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from nvfp4_w4a4_gemm_quantize_amd import binding as B
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.load()
+    S = setup(torch, B)
+    for i in range(args.warmup):
+        step(torch, B, S, i, None)
+    names = ["prefill", "gdn", "gate_up", "down", "decode_all", "decode"]
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(torch, B, S, i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dur = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}   # ms
+    prefill_flop = FLOP["gdn"] + FLOP["gate_up"] + FLOP["down"]
+    value = prefill_flop / (dur["prefill"] * 1e-3) / 1e12
+    gemm_ms = dur["gdn"] + dur["gate_up"] + dur["down"]
+    achieved = prefill_flop / (gemm_ms * 1e-3) / 1e12
+    sweep = decode_sweep(torch, B, S)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "hybrid-layer linear path: prefill M=4096 (GDN fused in-projection N=16480 K=5120 "
+                               "with 6 per-module global scales + MLP gate_up N=34816 SiLU*mul, h quantize, down "
+                               "K=17408) and decode M=1 (N=17408 K=5120)",
+                   "prefill_tokens": 4096, "decode_tokens": 1, "weights": "NVFP4 packed, 16-element E4M3 scales",
+                   "activations": "quantized per call (dynamic FP32 global scale)"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_prefill_kernel (3 launches per step)",
+                     "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "fp4_peak_frac_context": round(achieved / PEAK_FP4_TFLOPS, 4)},
+        "prefill_ms": {k: round(dur[k], 4) for k in ("prefill", "gdn", "gate_up", "down")},
+        "decode": {"M": 1, "gemm_us": round(dur["decode"] * 1e3, 2),
+                   "weight_GBps": round(DECODE_W_BYTES / (dur["decode"] * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(DECODE_BYTES / (dur["decode"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                   "quantize_plus_gemm_us": round(dur["decode_all"] * 1e3, 2),
+                   "sweep": sweep},
+        "setup_s": round(S["setup_s"], 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
