@@ -73,48 +73,173 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p, bool ok) {
 // Scale pair (blocks 2h, 2h+1 of a 64-wide K tile) -> scale byte for sub-step s.
 __device__ __forceinline__ uint32_t scale_byte(uint32_t pair, int s) { return (pair >> (8 * (s >> 1))) & 0xFFu; }
 
-// ------------------------------------------------------ prefill kernel ----
-// Workgroup tile BM x BN (BM = WM*MF*32, BN = WN*NF*32) over the whole K.
-// Per 64-wide K step the packed A rows and the W tiles are staged through LDS
-// (double buffered, 16-byte global loads held in registers while the current
-// stage is multiplied); each wave reads its fragments from LDS, dequantises
-// them in registers and issues MF*NF*4 MFMAs.
+// ------------------------------------------------------ tile epilogue ----
+// Epilogue of a workgroup tile: each 32x32 accumulator fragment of a wave goes
+// through a per-wave LDS staging tile (32 x 33 floats) so that every lane
+// owns 4 rows x 4 consecutive columns; it applies alpha and the column's gate
+// function and stores 4 contiguous outputs per row.  One runtime loop over
+// the fragments keeps the epilogue code single; the fragment to stage is
+// picked by compile-time cases, so the accumulators stay in registers.
+// col_base: first output column of the workgroup; wave_n's fragment jj covers
+// output columns col_base + (wave_n * NJ + jj) * 32 .. +31.
+template <int MF, int NF, int WM, int WN, bool SILU>
+__device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* lds, int lane, int wave,
+                                              int wave_m, int wave_n, int64_t m0, int64_t col_base,
+                                              int64_t m, int64_t n, void* out, const EpilogueArgs& epi) {
+  constexpr int EPI_STRIDE = 33;
+  constexpr int NJ = SILU ? NF / 2 : NF;
+  const int r = lane & 31, h = lane >> 5;
+  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * EPI_STRIDE);
+  const int er = (lane >> 3) * 4, ec = (lane & 7) * 4;   // this lane: rows er..er+3, cols ec..ec+3
+  const float ga = *epi.a_global;
+  const bool bf16 = epi.out_bf16 != 0;
+  const int64_t ld = epi.ld_out;
+  const int64_t ncols = SILU ? n / 2 : n;
+
+  auto stage_frag = [&](floatx16 f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ep[(8 * (e >> 2) + 4 * h + (e & 3)) * EPI_STRIDE + r] = f[e];
+  };
+  auto read_frag = [&](float (&v)[4][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v[a][b] = ep[(er + a) * EPI_STRIDE + ec + b];
+  };
+  auto store_row = [&](int64_t row, int64_t col0, const float (&v)[4]) __attribute__((always_inline)) {
+    if (row >= m) return;
+    const int64_t idx = row * ld + col0;
+    if (col0 + 3 < ncols && (idx & 3) == 0) {
+      if (bf16) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = pk;
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (col0 + b < ncols) store_out(out, bf16, idx + b, v[b]);
+    }
+  };
+
+  const float alpha_silu = SILU ? 1.0f / (ga * epi.seg_w_global[0]) : 0.0f;
+  for (int f = 0; f < NJ * MF; ++f) {
+    const int jj = f / MF, i = f % MF;
+    const int64_t col0 = col_base + (int64_t)(wave_n * NJ + jj) * 32 + ec;
+    float v[4][4];
+    __syncthreads();
+    static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
+      constexpr int F = decltype(c)::value;
+      if (f == F) stage_frag(acc[F % MF][F / MF]);
+    });
+    __syncthreads();
+    read_frag(v);
+    if constexpr (SILU) {
+      float u[4][4];
+      __syncthreads();
+      static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
+        constexpr int F = decltype(c)::value;
+        if (f == F) stage_frag(acc[F % MF][F / MF + NF / 2]);
+      });
+      __syncthreads();
+      read_frag(u);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v[a][b] = silu_mul(v[a][b] * alpha_silu, u[a][b] * alpha_silu);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const ColumnEpilogue ce = column_epilogue(epi, col0 + b < n ? col0 + b : n - 1, ga);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) v[a][b] = apply_epilogue(ce, v[a][b]);
+      }
+    }
+    const int64_t row0 = m0 + wave_m * MF * 32 + i * 32 + er;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) store_row(row0 + a, col0, v[a]);
+  }
+}
+
+// One 64-wide K step of a wave: MF x NF fragments, 4 sub-steps of 16 K each.
+// ac/bc: the lanes' 16 code bytes per fragment; asc/bsc: the lanes' two block
+// scales (bytes 0, 1) per fragment.
+template <int MF, int NF>
+__device__ __forceinline__ void mma_k64(floatx16 (&acc)[MF][NF], const uint4 (&ac)[MF], const uint32_t (&asc)[MF],
+                                        const uint4 (&bc)[NF], const uint32_t (&bsc)[NF]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    half8_t av[MF], bv[NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const uint32_t cw = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
+      av[i] = dequant8(cw, scale_pair_f16(scale_byte(asc[i], s)));
+    }
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const uint32_t cw = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
+      bv[j] = dequant8(cw, scale_pair_f16(scale_byte(bsc[j], s)));
+    }
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int j = 0; j < NF; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+  }
+}
+
+// --------------------------------------------- prefill kernel, any K ----
+// Register-staged variant for K % 64 == 32 (a half K tile at the end): every
+// load is guarded and zero-filled.  Workgroup tile BM x BN over the whole K;
+// per 64-wide K step the packed A rows and W tiles go global -> registers ->
+// LDS (double buffered) and each wave multiplies its fragments.
 // SILU: the workgroup covers BN/2 output columns o0.. and loads the matching
 // gate tiles (columns o0..) and up tiles (columns n/2 + o0..); frag j < NF/2
 // of a wave is a gate tile and frag j + NF/2 the up tile of the same columns.
+template <int MF, int NF, int WM, int WN>
+struct RegShape {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int BM = WM * MF * 32;
+  static constexpr int BN = WN * NF * 32;
+  static constexpr int NTILES = BN / 32;
+  static constexpr int HSTRIDE = BM * 16 + 64;        // LDS bytes per K half of the A stage
+  static constexpr int OFF_AS = 2 * HSTRIDE;
+  static constexpr int OFF_BC = OFF_AS + BM * 4;
+  static constexpr int OFF_BS = OFF_BC + NTILES * kTileCodeBytes;
+  static constexpr int STAGE = OFF_BS + NTILES * 128;
+  static constexpr int EPI_BYTES = WM * WN * 32 * 33 * 4;
+  static constexpr int LDS = (2 * STAGE > EPI_BYTES) ? 2 * STAGE : EPI_BYTES;
+};
+
 template <int MF, int NF, int WM, int WN, bool SILU>
 __global__ void __launch_bounds__(WM * WN * 64)
-gemm_prefill_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
-                    const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
-                    EpilogueArgs epi) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BM = WM * MF * 32;
-  constexpr int BN = WN * NF * 32;
-  constexpr int NTILES = BN / 32;
-  constexpr int HSTRIDE = BM * 16 + 64;             // LDS bytes per K half of the A stage
-  constexpr int A_CHUNKS = 2 * BM;                  // 16-byte chunks of A codes per stage
+gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
+                         const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
+                         EpilogueArgs epi) {
+  using P = RegShape<MF, NF, WM, WN>;
+  constexpr int NT = P::NT, BM = P::BM, BN = P::BN, NTILES = P::NTILES, HSTRIDE = P::HSTRIDE;
+  constexpr int A_CHUNKS = 2 * BM;
   constexpr int B_CHUNKS = NTILES * 64;
   constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
   constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
   constexpr int AS_PER_T = (BM + NT - 1) / NT;
   constexpr int BS_PER_T = (BN + NT - 1) / NT;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_ac[2][2 * HSTRIDE];
-  __shared__ uint32_t s_as[2][BM];
-  __shared__ __attribute__((aligned(16))) uint8_t s_bc[2][NTILES * kTileCodeBytes];
-  __shared__ uint32_t s_bs[2][NTILES * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[P::LDS];
 
   const int t = threadIdx.x;
   const int lane = t & 63, r = lane & 31, h = lane >> 5;
-  const int wave = t >> 6, wave_m = wave / WN, wave_n = wave % WN;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), wave_m = wave / WN, wave_n = wave % WN;
   const int64_t KT = (k + kTileK - 1) / kTileK;
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
-  const uint8_t* w_scales = w_packed + ((n + kTileN - 1) / kTileN) * kTileN * (KT * kTileK) / 2;
+  const uint8_t* w_scales = w_packed + ntiles_total * kTileN * (KT * kTileK) / 2;
   const bool k_aligned64 = (k & 63) == 0;
+  const int64_t o0 = SILU ? (int64_t)blockIdx.x * (BN / 2) : 0;
 
-  int64_t o0 = 0;  // SILU: first output column of the workgroup
   auto ntile_of = [&](int tl) -> int64_t {
     if (SILU) {
       const int half = NTILES / 2;
@@ -122,17 +247,13 @@ gemm_prefill_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restri
     }
     return (int64_t)blockIdx.x * NTILES + tl;
   };
-  bool tile_ok[NTILES];
-  if (SILU) o0 = (int64_t)blockIdx.x * (BN / 2);
-#pragma unroll
-  for (int tl = 0; tl < NTILES; ++tl) {
+  auto tile_ok = [&](int tl) -> bool {
     if (SILU) {
       const int half = NTILES / 2;
-      tile_ok[tl] = (o0 / 32 + (tl < half ? tl : tl - half)) < (n / 2) / 32;
-    } else {
-      tile_ok[tl] = ntile_of(tl) < ntiles_total;
+      return (o0 / 32 + (tl < half ? tl : tl - half)) < (n / 2) / 32;
     }
-  }
+    return ntile_of(tl) < ntiles_total;
+  };
 
   uint4 ra[A_PER_T], rb[B_PER_T];
   uint32_t ras[AS_PER_T], rbs[BS_PER_T];
@@ -164,7 +285,7 @@ gemm_prefill_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restri
     for (int i = 0; i < B_PER_T; ++i) {
       const int q = t + i * NT;
       const int tl = q >> 6, ln = q & 63;
-      const bool ok = q < B_CHUNKS && tile_ok[tl < NTILES ? tl : 0];
+      const bool ok = q < B_CHUNKS && tile_ok(tl);
       rb[i] = ld16(w_packed + (ntile_of(tl) * KT + kt) * kTileCodeBytes + ln * 16, ok);
     }
 #pragma unroll
@@ -172,31 +293,32 @@ gemm_prefill_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restri
       const int q = t + i * NT;
       const int tl = q >> 5, c = q & 31;
       uint32_t v = 0;
-      if (q < BN && tile_ok[tl < NTILES ? tl : 0])
+      if (q < BN && tile_ok(tl))
         v = *reinterpret_cast<const uint32_t*>(w_scales + (ntile_of(tl) * KT + kt) * kTileScaleBytes + c * 4);
       rbs[i] = v;
     }
   };
   auto sstore = [&](int stage) {
+    uint8_t* base = lds + stage * P::STAGE;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       const int q = t + i * NT;
-      if (q < A_CHUNKS) *reinterpret_cast<uint4*>(&s_ac[stage][(q & 1) * HSTRIDE + (q >> 1) * 16]) = ra[i];
+      if (q < A_CHUNKS) *reinterpret_cast<uint4*>(base + (q & 1) * HSTRIDE + (q >> 1) * 16) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < AS_PER_T; ++i) {
       const int row = t + i * NT;
-      if (row < BM) s_as[stage][row] = ras[i];
+      if (row < BM) reinterpret_cast<uint32_t*>(base + P::OFF_AS)[row] = ras[i];
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
       const int q = t + i * NT;
-      if (q < B_CHUNKS) *reinterpret_cast<uint4*>(&s_bc[stage][q * 16]) = rb[i];
+      if (q < B_CHUNKS) *reinterpret_cast<uint4*>(base + P::OFF_BC + q * 16) = rb[i];
     }
 #pragma unroll
     for (int i = 0; i < BS_PER_T; ++i) {
       const int q = t + i * NT;
-      if (q < BN) s_bs[stage][q] = rbs[i];
+      if (q < BN) reinterpret_cast<uint32_t*>(base + P::OFF_BS)[q] = rbs[i];
     }
   };
 
@@ -218,98 +340,280 @@ gemm_prefill_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restri
   __syncthreads();
   for (int64_t kt = 0; kt < KT; ++kt) {
     const int stage = (int)(kt & 1);
+    const uint8_t* base = lds + stage * P::STAGE;
     if (kt + 1 < KT) gload(kt + 1);
     uint4 ac[MF], bc[NF];
     uint32_t asc[MF], bsc[NF];
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int row = wave_m * MF * 32 + i * 32 + r;
-      ac[i] = *reinterpret_cast<const uint4*>(&s_ac[stage][h * HSTRIDE + row * 16]);
-      asc[i] = s_as[stage][row] >> (16 * h);
+      ac[i] = *reinterpret_cast<const uint4*>(base + h * HSTRIDE + row * 16);
+      asc[i] = reinterpret_cast<const uint32_t*>(base + P::OFF_AS)[row] >> (16 * h);
     }
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int tl = lds_tile(j);
-      bc[j] = *reinterpret_cast<const uint4*>(&s_bc[stage][tl * kTileCodeBytes + lane * 16]);
-      bsc[j] = s_bs[stage][tl * 32 + r] >> (16 * h);
+      bc[j] = *reinterpret_cast<const uint4*>(base + P::OFF_BC + tl * kTileCodeBytes + lane * 16);
+      bsc[j] = reinterpret_cast<const uint32_t*>(base + P::OFF_BS)[tl * 32 + r] >> (16 * h);
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      half8_t av[MF], bv[NF];
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        const uint32_t cw = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
-        av[i] = dequant8(cw, scale_pair_f16(scale_byte(asc[i], s)));
-      }
-#pragma unroll
-      for (int j = 0; j < NF; ++j) {
-        const uint32_t cw = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
-        bv[j] = dequant8(cw, scale_pair_f16(scale_byte(bsc[j], s)));
-      }
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int j = 0; j < NF; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
-    }
+    mma_k64<MF, NF>(acc, ac, asc, bc, bsc);
     if (kt + 1 < KT) sstore(stage ^ 1);
     __syncthreads();
   }
 
-  // Epilogue: alpha (per column segment), gate functions, store.
-  const float ga = *epi.a_global;
-  const bool bf16 = epi.out_bf16 != 0;
-  const int64_t row_base = m0 + wave_m * MF * 32 + 4 * h;
-  if (SILU) {
-    const float alpha = 1.0f / (ga * epi.seg_w_global[0]);
-#pragma unroll
-    for (int j = 0; j < NF / 2; ++j) {
-      const int64_t col = o0 + (int64_t)(wave_n * (NF / 2) + j) * 32 + r;
-      if (col >= n / 2) continue;
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (row < m) store_out(out, bf16, row * epi.ld_out + col,
-                                 silu_mul(acc[i][j][e] * alpha, acc[i][j + NF / 2][e] * alpha));
-        }
+  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds, lane, wave, wave_m, wave_n, m0,
+                                      SILU ? o0 : (int64_t)blockIdx.x * BN, m, n, out, epi);
+}
+
+// -------------------------------------- prefill kernel, K % 64 == 0 ----
+// Global -> LDS DMA pipeline with NSTAGE stages.  Every wave issues a fixed
+// set of global_load_lds (16-byte or 4-byte per lane) per stage straight into
+// a fragment-ordered LDS layout (1 KB per 32-row x 64-K fragment, lane l's 16
+// bytes at l*16 -- exactly where the MFMA operand read wants them), so no
+// registers or VALU are spent on staging.  Rows past m and weight tiles past
+// n are not masked: their addresses are clamped to the last valid row/tile,
+// which keeps every wave's load count fixed (the vmcnt accounting below
+// relies on it) and only feeds output rows/columns that are never stored.
+// Loads for stage kt+NSTAGE-1 are issued right after the barrier of step kt,
+// into the buffer step kt-1 has finished with.
+template <int MF, int NF, int WM, int WN, int NSTAGE>
+struct DmaShape {
+  static constexpr int NWAVES = WM * WN;
+  static constexpr int BM = WM * MF * 32;
+  static constexpr int BN = WN * NF * 32;
+  static constexpr int AFRAGS = BM / 32;
+  static constexpr int NTILES = BN / 32;
+  static constexpr int OFF_AS = AFRAGS * 1024;
+  static constexpr int OFF_BC = OFF_AS + BM * 4;
+  static constexpr int OFF_BS = OFF_BC + NTILES * 1024;
+  static constexpr int STAGE = OFF_BS + NTILES * 128;
+  static constexpr int N_AC = AFRAGS, N_AS = BM / 64, N_BC = NTILES, N_BS = NTILES / 2;
+  static constexpr int LOADS = N_AC + N_AS + N_BC + N_BS;
+  static constexpr int LPW = LOADS / NWAVES;            // DMA instructions per wave per stage
+  static constexpr int EPI_BYTES = NWAVES * 32 * 33 * 4;
+  static_assert(N_AC % NWAVES == 0 && N_AS % NWAVES == 0 && N_BC % NWAVES == 0 && N_BS % NWAVES == 0,
+                "each load class must split evenly over the waves");
+};
+
+// Global -> LDS DMA of 16 (or 4) bytes per lane: lane l's bytes land at
+// dst + l*16 (l*4).  Written as a single instruction in inline asm so the
+// compiler does not add its own (conservative, pipeline-draining) vmcnt waits
+// before later LDS reads; completion is tracked explicitly with wait_vmcnt
+// and published to the other waves with the barrier.  The instruction has no
+// register results (its data goes to LDS); the address registers are read at
+// issue.  M0 holds the wave-uniform LDS destination; the leading s_nop covers
+// the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ uint32_t lds_offset(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_offset(dst)) : "memory");
+}
+__device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_offset(dst)) : "memory");
+}
+// Compiler-only fence: no memory access is moved across it.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
+                        const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
+                        EpilogueArgs epi) {
+  using P = DmaShape<MF, NF, WM, WN, NSTAGE>;
+  constexpr int NWAVES = P::NWAVES, BM = P::BM, BN = P::BN, NTILES = P::NTILES;
+  static_assert(NSTAGE == 3 || NSTAGE == 4, "3 or 4 stages");
+  // One LDS object per stage: the compiler can then tell that the DMA into the
+  // stage being filled does not alias the reads of the stage being consumed
+  // and does not wait for it before those reads.
+  // (stage 0 starts 1 KB into its object: an LDS address of exactly 0 lets the
+  // compiler fold the offsets into bit operations that lose the alias
+  // information the DMA waits rely on)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[P::STAGE + 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[P::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[P::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[NSTAGE > 3 ? P::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_epi[P::EPI_BYTES];
+  auto buf = [&](auto b) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int B = decltype(b)::value;
+    if constexpr (B == 0) return lds_s0 + 1024;
+    else if constexpr (B == 1) return lds_s1;
+    else if constexpr (B == 2) return lds_s2;
+    else return lds_s3;
+  };
+
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_m = wave / WN, wave_n = wave % WN;
+  const int64_t KT = k / kTileK;
+  const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const uint32_t a_row_bytes = (uint32_t)(k / 2), a_row_scales = (uint32_t)(k / 16);
+  const uint8_t* w_scales = w_packed + ntiles_total * kTileN * k / 2;
+  const int64_t o0 = SILU ? (int64_t)blockIdx.x * (BN / 2) : 0;
+
+  auto ntile_of = [&](int tl) -> int64_t {
+    int64_t nt;
+    if (SILU) {
+      const int half = NTILES / 2;
+      nt = tl < half ? (o0 / 32 + tl) : ((n / 2 + o0) / 32 + (tl - half));
+    } else {
+      nt = (int64_t)blockIdx.x * NTILES + tl;
     }
-  } else {
+    return nt < ntiles_total ? nt : ntiles_total - 1;   // clamped: see the kernel comment
+  };
+  auto row_of = [&](int64_t row) -> int64_t { return row < m ? row : m - 1; };
+
+  // Per-lane source addresses (K step 0) and LDS offsets of this wave's loads.
+  // Load classes in order: A code fragments, A scale groups (64 rows), W tiles,
+  // W scale pairs; class sizes are multiples of the wave count, so load i of
+  // every wave belongs to the same class (known at compile time).
+  constexpr int I_AS = P::N_AC / NWAVES, I_BC = I_AS + P::N_AS / NWAVES, I_BS = I_BC + P::N_BC / NWAVES;
+  const uint8_t* src[P::LPW];
+  int dst[P::LPW];
 #pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      const int64_t col = ntile_of(wave_n * NF + j) * 32 + r;
-      if (col >= n) continue;
-      const ColumnEpilogue ce = column_epilogue(epi, col, ga);
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (row < m) store_out(out, bf16, row * epi.ld_out + col, apply_epilogue(ce, acc[i][j][e]));
-        }
+  for (int i = 0; i < P::LPW; ++i) {
+    const int q = wave + i * NWAVES;
+    if (i < I_AS) {
+      const int f = q;
+      src[i] = a_codes + row_of(m0 + 32 * f + r) * a_row_bytes + h * 16;
+      dst[i] = f * 1024;
+    } else if (i < I_BC) {
+      const int g = q - P::N_AC;
+      src[i] = a_scales + row_of(m0 + 64 * g + lane) * a_row_scales;
+      dst[i] = P::OFF_AS + g * 256;
+    } else if (i < I_BS) {
+      const int tl = q - P::N_AC - P::N_AS;
+      src[i] = w_packed + ntile_of(tl) * KT * kTileCodeBytes + lane * 16;
+      dst[i] = P::OFF_BC + tl * 1024;
+    } else {
+      const int p = q - P::N_AC - P::N_AS - P::N_BC;
+      const int tl = 2 * p + h;
+      src[i] = w_scales + ntile_of(tl) * KT * kTileScaleBytes + r * 4;
+      dst[i] = P::OFF_BS + p * 256;
     }
   }
+  // Stages are issued strictly in order, so each load keeps a running source
+  // pointer that advances by its per-stage stride after every issue.
+  auto issue = [&](uint8_t* base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < P::LPW; ++i) {
+      if (i < I_AS) { dma16(src[i], base + dst[i]); src[i] += 32; }
+      else if (i < I_BC) { dma4(src[i], base + dst[i]); src[i] += 4; }
+      else if (i < I_BS) { dma16(src[i], base + dst[i]); src[i] += kTileCodeBytes; }
+      else { dma4(src[i], base + dst[i]); src[i] += kTileScaleBytes; }
+    }
+  };
+
+  floatx16 acc[MF][NF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  auto lds_tile = [&](int j) -> int {
+    if (SILU) return j < NF / 2 ? wave_n * (NF / 2) + j : NTILES / 2 + wave_n * (NF / 2) + (j - NF / 2);
+    return wave_n * NF + j;
+  };
+
+  // One K step: wait for its stage, barrier, read the wave's fragments,
+  // optionally issue the DMA of stage kt+NSTAGE-1, multiply.
+  auto kstep = [&](auto b, int64_t kt, bool do_issue, auto waitn) __attribute__((always_inline)) {
+    constexpr int B = decltype(b)::value;
+    wait_vmcnt<decltype(waitn)::value>();
+    // A bare barrier (no memory fence): the DMA of this stage is covered by the
+    // vmcnt wait above, and the previous stage's LDS reads have all been
+    // consumed by that step's MFMAs, so no further waits are needed.
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    const uint8_t* base = buf(b);
+    uint4 ac[MF], bc[NF];
+    uint32_t asc[MF], bsc[NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int f = wave_m * MF + i;
+      ac[i] = *reinterpret_cast<const uint4*>(base + f * 1024 + lane * 16);
+      asc[i] = reinterpret_cast<const uint32_t*>(base + P::OFF_AS)[f * 32 + r] >> (16 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int tl = lds_tile(j);
+      bc[j] = *reinterpret_cast<const uint4*>(base + P::OFF_BC + tl * 1024 + lane * 16);
+      bsc[j] = reinterpret_cast<const uint32_t*>(base + P::OFF_BS)[tl * 32 + r] >> (16 * h);
+    }
+    // The next stage's loads go out after this stage's reads are issued.
+    if (do_issue) issue(buf(std::integral_constant<int, (B + NSTAGE - 1) % NSTAGE>{}));
+    mma_k64<MF, NF>(acc, ac, asc, bc, bsc);
+  };
+
+  // Prologue: stages 0..NSTAGE-2 (the launcher guarantees KT >= NSTAGE).
+  static_for<0, NSTAGE - 1>([&](auto s) __attribute__((always_inline)) { issue(buf(s)); });
+  // Steady state, in groups of NSTAGE steps with compile-time buffers; every
+  // step issues, so the in-flight DMA pattern is the same at every step.
+  int64_t kt0 = 0;
+  for (; kt0 + 2 * NSTAGE - 2 < KT; kt0 += NSTAGE) {
+    static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
+      kstep(b, kt0 + decltype(b)::value, true, std::integral_constant<int, P::LPW * (NSTAGE - 2)>{});
+    });
+  }
+  // Tail: the last 2*NSTAGE-2 or fewer steps.  kt0 is a multiple of NSTAGE, so
+  // the buffers are again compile-time; loads are issued while stages remain
+  // and every step waits for all in-flight loads (a handful of steps).
+  for (; kt0 < KT; kt0 += NSTAGE) {
+    static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
+      const int64_t kt = kt0 + decltype(b)::value;
+      if (kt < KT) kstep(b, kt, kt + NSTAGE - 1 < KT, std::integral_constant<int, 0>{});
+    });
+  }
+
+  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds_epi, lane, wave, wave_m, wave_n, m0,
+                                      SILU ? o0 : (int64_t)blockIdx.x * BN, m, n, out, epi);
 }
 
 // ------------------------------------------------------- decode kernel ----
 // m <= 64: weight streaming.  One workgroup per 32-column weight slab (two
-// slabs -- gate and up -- for SILU); its 4 waves split K four ways, each
+// slabs -- gate and up -- for SILU); its waves split K evenly, each
 // streaming its part of the slab straight from HBM into registers with one
 // 16-byte load per lane per 64-wide K tile (the packed layout is already in
-// MFMA lane order), with the next tile's loads issued before the current
-// tile is multiplied.  The four partial accumulators are summed in LDS in a
-// fixed order.
-template <int MFD, bool SILU>
-__global__ void __launch_bounds__(256)
+// MFMA lane order).  Loads run up to eight tiles ahead of the MFMAs.
+// ALDS (small m*k): the workgroup first dequantises A once into LDS as f16 in
+// MFMA operand order (rows < m only; lanes of absent rows read a zero slot),
+// so the loop spends VALU only on the weights.  Otherwise A is dequantised
+// per tile in registers.  The waves' partial accumulators are summed in LDS in
+// a fixed order.
+constexpr int kDecodeALdsBytes = 48 * 1024;
+#ifndef NVFP4_DECODE_GROUP_A
+#define NVFP4_DECODE_GROUP_A 6
+#endif
+// Tiles per load group with A staged in LDS (two groups are in flight; six is
+// the most that fits three waves per SIMD without spilling).
+constexpr int kDecodeGroupA = NVFP4_DECODE_GROUP_A;
+
+// Sized so that three 4-wave workgroups fit on a CU (<= 168 VGPRs per wave,
+// A staging in dynamic LDS of exactly (m+1)*k*2 bytes): the 544 workgroups of
+// a 17408-column projection are then all resident at once instead of the
+// last few running as a second round.
+template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U>
+__global__ void __launch_bounds__(DW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
                    const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
                    EpilogueArgs epi) {
   constexpr int NS = SILU ? 2 : 1;                 // weight slabs per workgroup
   constexpr int NACC = MFD * NS;
-  __shared__ float s_red[3][NACC][16][64];
+  __shared__ float s_red[DW - 1][NACC][16][64];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_a[];    // ALDS: (m+1)*k*2 bytes
 
   const int t = threadIdx.x;
-  const int lane = t & 63, r = lane & 31, h = lane >> 5, wave = t >> 6;
+  const int lane = t & 63, r = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t KT = (k + kTileK - 1) / kTileK;
   const int64_t np = (n + kTileN - 1) / kTileN * kTileN;
   const uint8_t* w_scales = w_packed + np * (KT * kTileK) / 2;
@@ -317,39 +621,63 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   int64_t slab[NS];
   slab[0] = blockIdx.x;
   if (SILU) slab[NS - 1] = blockIdx.x + (n / 2) / kTileN;
-  const int64_t kt0 = KT * wave / 4, kt1 = KT * (wave + 1) / 4;
+  const int64_t kt0 = KT * wave / DW, kt1 = KT * (wave + 1) / DW;
 
-  floatx16 acc[MFD][NS];
+  // Independent accumulators per K sub-step break the MFMA dependency chain
+  // (a single 32x32 output tile would otherwise serialise every MFMA).
+  constexpr int NSUB = 2;
+  floatx16 part[MFD][NS][NSUB];
 #pragma unroll
   for (int i = 0; i < MFD; ++i)
 #pragma unroll
     for (int j = 0; j < NS; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  struct Tile { uint4 a[MFD]; uint32_t as[MFD]; uint4 b[NS]; uint32_t bs[NS]; };
-  auto load = [&](int64_t kt, Tile& T) {
+      for (int q = 0; q < NSUB; ++q)
 #pragma unroll
-    for (int i = 0; i < MFD; ++i) {
-      const int64_t row = i * 32 + r;
-      const bool ok = row < m && (kt * 64 + h * 32) < k;
-      T.a[i] = ld16(a_codes + row * a_row_bytes + kt * 32 + h * 16, ok);
-      T.as[i] = ok ? *reinterpret_cast<const uint16_t*>(a_scales + row * a_row_scales + kt * 4 + 2 * h) : 0u;
+        for (int e = 0; e < 16; ++e) part[i][j][q][e] = 0.0f;
+
+  // Per-lane constant offsets; per-tile bases are wave-uniform (scalar).
+  const uint32_t w_lane = lane * 16, ws_lane = r * 4 + 2 * h;
+  // A in LDS (ALDS): 16-byte chunk (kt, s, hh, row) at ((kt*4 + s)*2 + hh)*(m+1) + row,
+  // row m of every group is zero; lanes of rows >= m read it.
+  const int64_t a_rows = m + 1;
+  const uint32_t a_lane = (uint32_t)((h * a_rows + (r < m ? r : m)) * 16);
+
+  struct Tile { uint4 a[ALDS ? 1 : MFD]; uint32_t as[ALDS ? 1 : MFD]; uint4 b[NS]; uint32_t bs[NS]; };
+  // Loads are unconditional (no branches, so the compiler can count them and
+  // wait only for the group about to be multiplied); tiles past the wave's
+  // range are clamped to its last tile and never multiplied.
+  auto load = [&](int64_t kt, Tile& T) __attribute__((always_inline)) {
+    kt = kt < kt1 ? kt : kt1 - 1;
+    if constexpr (!ALDS) {
+#pragma unroll
+      for (int i = 0; i < MFD; ++i) {
+        const int64_t row = i * 32 + r;
+        const bool ok = row < m && (kt * 64 + h * 32) < k;
+        T.a[i] = ld16(a_codes + row * a_row_bytes + kt * 32 + h * 16, ok);
+        T.as[i] = ok ? *reinterpret_cast<const uint16_t*>(a_scales + row * a_row_scales + kt * 4 + 2 * h) : 0u;
+      }
     }
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + (slab[j] * KT + kt) * kTileCodeBytes + lane * 16);
-      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_scales + (slab[j] * KT + kt) * kTileScaleBytes + r * 4 + 2 * h);
+      const int64_t tile = slab[j] * KT + kt;                      // wave-uniform
+      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile * kTileCodeBytes + w_lane);
+      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_scales + tile * kTileScaleBytes + ws_lane);
     }
   };
-  auto compute = [&](const Tile& T) {
+  auto compute = [&](int64_t kt, const Tile& T) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       half8_t av[MFD], bv[NS];
+      if constexpr (ALDS) {
+        const uint32_t grp = (uint32_t)((kt * 4 + s) * 2 * a_rows * 16);   // wave-uniform
+        av[0] = *reinterpret_cast<const half8_t*>(s_a + grp + a_lane);
+      } else {
 #pragma unroll
-      for (int i = 0; i < MFD; ++i) {
-        const uint32_t cw = s == 0 ? T.a[i].x : s == 1 ? T.a[i].y : s == 2 ? T.a[i].z : T.a[i].w;
-        av[i] = dequant8(cw, scale_pair_f16(scale_byte(T.as[i], s)));
+        for (int i = 0; i < MFD; ++i) {
+          const uint32_t cw = s == 0 ? T.a[i].x : s == 1 ? T.a[i].y : s == 2 ? T.a[i].z : T.a[i].w;
+          av[i] = dequant8(cw, scale_pair_f16(scale_byte(T.as[i], s)));
+        }
       }
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -359,19 +687,63 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 #pragma unroll
       for (int i = 0; i < MFD; ++i)
 #pragma unroll
-        for (int j = 0; j < NS; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < NS; ++j) part[i][j][s % NSUB] = mfma32x32x16(av[i], bv[j], part[i][j][s % NSUB]);
     }
   };
+  auto load_group = [&](int64_t g0, Tile (&T)[U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(g0 + u, T[u]);
+  };
+  auto compute_group = [&](int64_t g0, const Tile (&T)[U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (g0 + u < kt1) compute(g0 + u, T[u]);
+  };
+
+  // The first weight group is requested before A is staged, so its latency
+  // overlaps the staging.
+  Tile g_a[U], g_b[U];
+  if (kt0 < kt1) load_group(kt0, g_a);
+  // Stage A into LDS once per workgroup (ALDS): dequantised f16 chunks in MFMA
+  // operand order plus one zero row per (kt, s, hh) group.
+  if constexpr (ALDS) {
+    const int64_t items = a_rows * KT * 2;         // (row, kt, hh): 32 values each
+    for (int64_t it = t; it < items; it += DW * 64) {
+      const int64_t row = it / (KT * 2), rem = it % (KT * 2), kt = rem >> 1, hh = rem & 1;
+      uint4 c = make_uint4(0u, 0u, 0u, 0u);
+      uint32_t sp = 0;
+      if (row < m && kt * 64 + hh * 32 < k) {
+        c = *reinterpret_cast<const uint4*>(a_codes + row * a_row_bytes + kt * 32 + hh * 16);
+        sp = *reinterpret_cast<const uint16_t*>(a_scales + row * a_row_scales + kt * 4 + 2 * hh);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t cw = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+        *reinterpret_cast<half8_t*>(s_a + (((kt * 4 + s) * 2 + hh) * a_rows + row) * 16) =
+            dequant8(cw, scale_pair_f16(scale_byte(sp, s)));
+      }
+    }
+    __syncthreads();
+  }
 
   if (kt0 < kt1) {
-    Tile cur, nxt;
-    load(kt0, cur);
-    for (int64_t kt = kt0; kt < kt1; ++kt) {
-      if (kt + 1 < kt1) load(kt + 1, nxt);
-      compute(cur);
-      cur = nxt;
+    for (int64_t g = kt0; g < kt1; g += 2 * U) {
+      load_group(g + U, g_b);
+      compute_group(g, g_a);
+      load_group(g + 2 * U, g_a);
+      compute_group(g + U, g_b);
     }
   }
+
+  floatx16 acc[MFD][NS];
+#pragma unroll
+  for (int i = 0; i < MFD; ++i)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      acc[i][j] = part[i][j][0];
+#pragma unroll
+      for (int q = 1; q < NSUB; ++q) acc[i][j] += part[i][j][q];
+    }
 
   if (wave > 0) {
 #pragma unroll
@@ -384,7 +756,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < 3; ++w)
+  for (int w = 0; w < DW - 1; ++w)
 #pragma unroll
     for (int i = 0; i < MFD; ++i)
 #pragma unroll
@@ -421,39 +793,75 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 }
 
 // ------------------------------------------------------------ launcher ----
+// Prefill tile: MF, NF (32x32 fragments per wave along M, N), WM, WN (waves), stages.
+#ifndef NVFP4_PREFILL_TILE
+#define NVFP4_PREFILL_TILE 4, 4, 2, 2
+#endif
+#ifndef NVFP4_PREFILL_STAGES
+#define NVFP4_PREFILL_STAGES 4
+#endif
+
 template <int MF, int NF, int WM, int WN>
 static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
                            int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   constexpr int BM = WM * MF * 32, BN = WN * NF * 32;
+  constexpr int NS = NVFP4_PREFILL_STAGES;
   const int64_t cols = epi.silu_mul ? n / 2 : n;
   const int64_t bn = epi.silu_mul ? BN / 2 : BN;
   dim3 grid((unsigned)((cols + bn - 1) / bn), (unsigned)((m + BM - 1) / BM));
-  if (epi.silu_mul)
-    hipLaunchKernelGGL((gemm_prefill_kernel<MF, NF, WM, WN, true>), grid, dim3(WM * WN * 64), 0, st,
-                       ac, as, m, w, n, k, out, epi);
-  else
-    hipLaunchKernelGGL((gemm_prefill_kernel<MF, NF, WM, WN, false>), grid, dim3(WM * WN * 64), 0, st,
-                       ac, as, m, w, n, k, out, epi);
+  dim3 block(WM * WN * 64);
+  if ((k & 63) == 0 && k / kTileK >= NS) {
+    if (epi.silu_mul)
+      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, true>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
+    else
+      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, false>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
+  } else {
+    if (epi.silu_mul)
+      hipLaunchKernelGGL((gemm_prefill_regs_kernel<MF, NF, WM, WN, true>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
+    else
+      hipLaunchKernelGGL((gemm_prefill_regs_kernel<MF, NF, WM, WN, false>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
+  }
+}
+
+// Decode launch shapes: every workgroup of a large projection must be resident
+// at once (544 of them for N = 17408), so the number of waves per workgroup
+// (the K split) and the register budget (waves per SIMD) are chosen together.
+template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U>
+static void launch_decode_kernel(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
+                                 int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+  const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
+  const unsigned lds = ALDS ? (unsigned)((m + 1) * ((k + kTileK - 1) / kTileK) * kTileK * 2) : 0u;
+  hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U>), dim3((unsigned)slabs), dim3(DW * 64), lds, st,
+                     ac, as, m, w, n, k, out, epi);
+}
+
+template <int MFD, bool SILU>
+static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
+                          int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+  if constexpr (MFD == 1 && !SILU) {
+    if ((m + 1) * k * 2 <= kDecodeALdsBytes)
+      launch_decode_kernel<1, false, true, 4, 3, kDecodeGroupA>(ac, as, m, w, n, k, out, epi, st);
+    else
+      launch_decode_kernel<1, false, false, 4, 3, 4>(ac, as, m, w, n, k, out, epi, st);
+  } else if constexpr (MFD == 2 && SILU) {
+    launch_decode_kernel<2, true, false, 2, 1, 4>(ac, as, m, w, n, k, out, epi, st);
+  } else {
+    launch_decode_kernel<MFD, SILU, false, 2, 2, 4>(ac, as, m, w, n, k, out, epi, st);
+  }
 }
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   if (m <= 64) {
-    const int64_t slabs = epi.silu_mul ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
-    dim3 grid((unsigned)slabs);
     if (m <= 32) {
-      if (epi.silu_mul)
-        hipLaunchKernelGGL((gemm_decode_kernel<1, true>), grid, dim3(256), 0, st, a_codes, a_scales, m, w_packed, n, k, out, epi);
-      else
-        hipLaunchKernelGGL((gemm_decode_kernel<1, false>), grid, dim3(256), 0, st, a_codes, a_scales, m, w_packed, n, k, out, epi);
+      if (epi.silu_mul) launch_decode<1, true>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
+      else launch_decode<1, false>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
     } else {
-      if (epi.silu_mul)
-        hipLaunchKernelGGL((gemm_decode_kernel<2, true>), grid, dim3(256), 0, st, a_codes, a_scales, m, w_packed, n, k, out, epi);
-      else
-        hipLaunchKernelGGL((gemm_decode_kernel<2, false>), grid, dim3(256), 0, st, a_codes, a_scales, m, w_packed, n, k, out, epi);
+      if (epi.silu_mul) launch_decode<2, true>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
+      else launch_decode<2, false>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
     }
   } else {
-    launch_prefill<2, 2, 2, 2>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
+    launch_prefill<NVFP4_PREFILL_TILE>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
   }
   return hipGetLastError();
 }

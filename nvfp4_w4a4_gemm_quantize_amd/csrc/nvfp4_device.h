@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nvfp4 {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -125,6 +127,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
   return v;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).  Used
+// where indices into accumulator arrays must stay compile-time constants.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // --------------------------------------------------- packed weight layout ----
