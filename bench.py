@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    p.add_argument("--no-decode-sweep", action="store_true", help="skip the per-M decode sweep (profiling runs)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
 
 
@@ -129,36 +132,69 @@ def step(torch, B, S, it, ev):
     rec("decode_all", 1)
 
 
-def decode_sweep(torch, B, S, iters=50):
-    """Weight GB/s of the decode GEMM at each M (rotating weight copies), after the timed region."""
+def _graph(torch, fn):
+    """Capture fn() (a sequence of library calls on the current stream) into a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                                    # warm-up on the capture stream's side, as torch requires
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def _replay_us(torch, g, calls, reps=3):
+    """Mean time per captured call over `reps` replays, from events around each replay."""
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1000 / calls)
+    return min(ts)
+
+
+def decode_sweep(torch, B, S, iters=64):
+    """Decode GEMM time at each M, from HIP-graph replays of `iters` back-to-back launches over the
+    rotating weight copies (a Python launch loop would measure the host, not the kernel).  Each
+    replayed output is checked bit-for-bit against an eager launch of the same call."""
     from nvfp4_w4a4_gemm_quantize_amd import inputs
     out = {}
     for M in inputs.DECODE_M:
         a = dev_bf16(torch, inputs.decode(M, weights=False)["A"])
         qc, qs, qg = B.nvfp4_quantize(a)
         y = torch.empty((M, 17408), dtype=torch.bfloat16, device="cuda")
-        for i in range(5):
-            B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(iters):
-            B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
-        e1.record()
-        q0.record()
-        for i in range(iters):
-            B.nvfp4_quantize(a, qg, True, qc, qs)
-            B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
-        q1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1000 / iters
-        us_q = q0.elapsed_time(q1) * 1000 / iters
+        last = S["dec_packed"][(iters - 1) % DECODE_COPIES]
+        B.gemm_w4a4(qc, qs, qg, last, S["dec_g"], 17408, 5120, out=y)
+        y_eager = y.clone()
+
+        def gemms():
+            for i in range(iters):
+                B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
+
+        def quant_gemms():
+            for i in range(iters):
+                B.nvfp4_quantize(a, qg, True, qc, qs)
+                B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
+
+        g1, g2 = _graph(torch, gemms), _graph(torch, quant_gemms)
+        us = _replay_us(torch, g1, iters)
+        same = bool(torch.equal(y, y_eager))
+        us_q = _replay_us(torch, g2, iters)
+        same = same and bool(torch.equal(y, y_eager))
         nbytes = DECODE_W_BYTES + M * (5120 * 9 // 16) + M * 17408 * 2
         out["M%d" % M] = {"gemm_us": round(us, 2), "weight_GBps": round(DECODE_W_BYTES / us / 1e3, 1),
                           "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 3),
                           "quantize_plus_gemm_us": round(us_q, 2),
-                          "tflops": round(2 * M * 17408 * 5120 / us / 1e6, 2)}
+                          "tflops": round(2 * M * 17408 * 5120 / us / 1e6, 2),
+                          "graph_replay_matches_eager": same}
+        del g1, g2
     return out
 
 
@@ -196,6 +232,49 @@ def cpu_baseline(target_s):
                       "%.1f s" % (rows_done, spent)}
 
 
+KERNEL_SOURCES = ("nvfp4_w4a4_gemm_quantize_amd/csrc/gemm.hip", "nvfp4_w4a4_gemm_quantize_amd/csrc/nvfp4_device.h",
+                  "nvfp4_w4a4_gemm_quantize_amd/csrc/kernels.h")
+TRAFFIC_PROFILE = "profiles/hbm_traffic__gemm_prefill_dma_kernel__prefill_M4096.txt"
+# Algorithmic bytes per launch: packed A + packed W + output (bf16).
+ALGO_BYTES = {
+    "gdn": 4096 * 5120 * 9 // 16 + 16480 * 5120 * 9 // 16 + 4096 * 16480 * 2,
+    "gate_up": 4096 * 5120 * 9 // 16 + 34816 * 5120 * 9 // 16 + 4096 * 17408 * 2,
+    "down": 4096 * 17408 * 9 // 16 + 5120 * 17408 * 9 // 16 + 4096 * 5120 * 2,
+}
+
+
+def kernel_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per prefill GEMM launch from the committed FETCH_SIZE/WRITE_SIZE summary (copy-calibrated),
+    or None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    sha, per = None, {}
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 2 and f[0] == "source_sha256":
+            sha = f[1]
+        elif len(f) >= 2 and f[0] == "launch":
+            kv = dict(zip(f[2::2], f[3::2]))
+            per[f[1]] = float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    if sha != kernel_source_sha256() or set(per) != set(ALGO_BYTES):
+        return None
+    return per
+
+
+def progress(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -209,6 +288,7 @@ def main():
         sys.exit(1)
     B.load()
     S = setup(torch, B)
+    progress("inputs packed and resident (%.1f s)" % S["setup_s"])
     for i in range(args.warmup):
         step(torch, B, S, i, None)
     names = ["prefill", "gdn", "gate_up", "down", "decode_all", "decode"]
@@ -220,12 +300,24 @@ def main():
         step(torch, B, S, i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    progress("%d timed steps done" % args.steps)
     dur = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}   # ms
     prefill_flop = FLOP["gdn"] + FLOP["gate_up"] + FLOP["down"]
     value = prefill_flop / (dur["prefill"] * 1e-3) / 1e12
     gemm_ms = dur["gdn"] + dur["gate_up"] + dur["down"]
     achieved = prefill_flop / (gemm_ms * 1e-3) / 1e12
-    sweep = decode_sweep(torch, B, S)
+    sweep = None if args.no_decode_sweep else decode_sweep(torch, B, S)
+    traffic = measured_traffic()
+    progress("decode sweep done")
+    if args.copy_probe_mib > 0:
+        # Untimed plain device copy of known size: the reference point that scales the HBM byte counters.
+        nb = args.copy_probe_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -244,9 +336,13 @@ def main():
                                "K=17408) and decode M=1 (N=17408 K=5120)",
                    "prefill_tokens": 4096, "decode_tokens": 1, "weights": "NVFP4 packed, 16-element E4M3 scales",
                    "activations": "quantized per call (dynamic FP32 global scale)"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_prefill_kernel (3 launches per step)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "gemm_prefill_dma_kernel (3 launches per step: gdn, gate_up, down)",
                      "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": None if traffic is None else int(sum(traffic.values()) / 3),
+                     "traffic_per": "HBM bytes per launch (mean of the 3), FETCH_SIZE + WRITE_SIZE, copy-calibrated",
+                     "algorithmic_bytes": int(sum(ALGO_BYTES.values()) / 3),
                      "fp4_peak_frac_context": round(achieved / PEAK_FP4_TFLOPS, 4)},
         "prefill_ms": {k: round(dur[k], 4) for k in ("prefill", "gdn", "gate_up", "down")},
         "decode": {"M": 1, "gemm_us": round(dur["decode"] * 1e3, 2),
@@ -257,6 +353,7 @@ def main():
         "setup_s": round(S["setup_s"], 1),
     }
     if not args.no_cpu_baseline:
+        progress("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -168,6 +168,40 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
 // ac/bc: the lanes' 16 code bytes per fragment; asc/bsc: the lanes' two block
 // scales (bytes 0, 1) per fragment.
 template <int MF, int NF>
+__device__ __forceinline__ void dequant_step(int s, const uint4 (&ac)[MF], const uint32_t (&asc)[MF],
+                                             const uint4 (&bc)[NF], const uint32_t (&bsc)[NF], half8_t (&av)[MF],
+                                             half8_t (&bv)[NF]) {
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const uint32_t cw = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
+    av[i] = dequant8(cw, scale_pair_f16(scale_byte(asc[i], s)));
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const uint32_t cw = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
+    bv[j] = dequant8(cw, scale_pair_f16(scale_byte(bsc[j], s)));
+  }
+}
+
+// As dequant_step, with whole scale dwords: the lane's pair starts at bit hsh.
+template <int MF, int NF>
+__device__ __forceinline__ void dequant_step_h(uint32_t hsh, int s, const uint4 (&ac)[MF], const uint32_t (&asc)[MF],
+                                               const uint4 (&bc)[NF], const uint32_t (&bsc)[NF], half8_t (&av)[MF],
+                                               half8_t (&bv)[NF]) {
+  const uint32_t off = hsh + 8u * (uint32_t)(s >> 1);
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const uint32_t cw = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
+    av[i] = dequant8(cw, scale_pair_f16(__builtin_amdgcn_ubfe(asc[i], off, 8)));
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const uint32_t cw = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
+    bv[j] = dequant8(cw, scale_pair_f16(__builtin_amdgcn_ubfe(bsc[j], off, 8)));
+  }
+}
+
+template <int MF, int NF>
 __device__ __forceinline__ void mma_k64(floatx16 (&acc)[MF][NF], const uint4 (&ac)[MF], const uint32_t (&asc)[MF],
                                         const uint4 (&bc)[NF], const uint32_t (&bsc)[NF]) {
 #pragma unroll
@@ -376,6 +410,12 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
 // relies on it) and only feeds output rows/columns that are never stored.
 // Loads for stage kt+NSTAGE-1 are issued right after the barrier of step kt,
 // into the buffer step kt-1 has finished with.
+// VALU ops issued after each MFMA in the pipelined main loop (0: the
+// unpipelined loop).
+#ifndef NVFP4_XPIPE
+#define NVFP4_XPIPE 5
+#endif
+
 template <int MF, int NF, int WM, int WN, int NSTAGE>
 struct DmaShape {
   static constexpr int NWAVES = WM * WN;
@@ -523,6 +563,120 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     return wave_n * NF + j;
   };
 
+#if NVFP4_XPIPE > 0
+#ifndef NVFP4_LATE
+#define NVFP4_LATE 3
+#endif
+  // Software pipeline across K steps.  Within step kt the four 16-wide
+  // sub-steps multiply operands that were dequantised during the previous
+  // sub-step, so the VALU work issues in the MFMA shadow.  Between sub-steps
+  // 2 and 3 (the step's fragments are all dequantised by then) the wave waits
+  // for stage kt+1, joins the barrier, reads its fragments of stage kt+1 and
+  // refills buffer kt % NSTAGE (read before this barrier by every wave) with
+  // stage kt + NSTAGE; sub-step 3 dequantises the first sub-step of kt+1.
+  // Raw fragments of one stage: code bytes and the whole scale dword of the
+  // lane's row (this lane's two blocks are its half h, picked at dequant time,
+  // so no VALU op depends on the LDS reads before the next sub-step starts).
+  struct Raw { uint4 ac[MF], bc[NF]; uint32_t asc[MF], bsc[NF]; };
+  auto read_frags = [&](const uint8_t* base, Raw& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int f = wave_m * MF + i;
+      R.ac[i] = *reinterpret_cast<const uint4*>(base + f * 1024 + lane * 16);
+      R.asc[i] = reinterpret_cast<const uint32_t*>(base + P::OFF_AS)[f * 32 + r];
+    }
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int tl = lds_tile(j);
+      R.bc[j] = *reinterpret_cast<const uint4*>(base + P::OFF_BC + tl * 1024 + lane * 16);
+      R.bsc[j] = reinterpret_cast<const uint32_t*>(base + P::OFF_BS)[tl * 32 + r];
+    }
+  };
+  const uint32_t hsh = 16u * h;   // bit offset of this lane's scale pair
+  auto mma = [&](const half8_t (&av)[MF], const half8_t (&bv)[NF]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int j = 0; j < NF; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+  };
+  // One MFMA, then a few VALU ops, for every MFMA of a sub-step.
+  auto interleave = [&]() __attribute__((always_inline)) {
+    static_for<0, MF * NF>([&](auto) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_XPIPE, 0);
+    });
+  };
+  auto sync_stage = [&](auto waitn) __attribute__((always_inline)) {
+    wait_vmcnt<decltype(waitn)::value>();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+  };
+
+  Raw R;
+  half8_t oa0[MF], ob0[NF], oa1[MF], ob1[NF];
+  // Prologue: all NSTAGE stages in flight (the launcher guarantees KT >= NSTAGE),
+  // then stage 0 is read and its first sub-step dequantised.
+  static_for<0, NSTAGE>([&](auto s) __attribute__((always_inline)) { issue(buf(s)); });
+  sync_stage(std::integral_constant<int, P::LPW * (NSTAGE - 1)>{});
+  read_frags(buf(std::integral_constant<int, 0>{}), R);
+  dequant_step_h<MF, NF>(hsh, 0, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
+
+  // Sub-step 3 follows the LDS reads of the next stage: its first MFMAs go out
+  // before any VALU op that needs the new fragments.
+  auto interleave_late = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NVFP4_LATE, 0);
+    static_for<0, MF * NF - NVFP4_LATE>([&](auto) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_XPIPE + 1, 0);
+    });
+  };
+
+  // Each sub-step is its own scheduling region (sched_barrier), so the
+  // compiler cannot drift the LDS reads or a dequantisation across sub-steps.
+  auto fence_sched = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+  auto kstep = [&](auto b, bool has_next, bool do_issue, auto waitn) __attribute__((always_inline)) {
+    constexpr int B = decltype(b)::value;
+    fence_sched();
+    dequant_step_h<MF, NF>(hsh, 1, R.ac, R.asc, R.bc, R.bsc, oa1, ob1);
+    mma(oa0, ob0);
+    interleave();
+    fence_sched();
+    dequant_step_h<MF, NF>(hsh, 2, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
+    mma(oa1, ob1);
+    interleave();
+    fence_sched();
+    dequant_step_h<MF, NF>(hsh, 3, R.ac, R.asc, R.bc, R.bsc, oa1, ob1);
+    mma(oa0, ob0);
+    interleave();
+    fence_sched();
+    // The current fragments are dead here, so the next stage's can be read.
+    if (has_next) {
+      sync_stage(waitn);
+      read_frags(buf(std::integral_constant<int, (B + 1) % NSTAGE>{}), R);
+      if (do_issue) issue(buf(b));
+      fence_sched();
+      dequant_step_h<MF, NF>(hsh, 0, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
+    }
+    mma(oa1, ob1);
+    interleave_late();
+  };
+  // Steady state, NSTAGE steps per iteration (compile-time buffers); every step
+  // issues a stage, so each waits with NSTAGE-2 stages still in flight.
+  int64_t kt0 = 0;
+  for (; kt0 + 2 * NSTAGE - 1 < KT; kt0 += NSTAGE) {
+    static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
+      kstep(b, true, true, std::integral_constant<int, P::LPW * (NSTAGE - 2)>{});
+    });
+  }
+  // Tail: the last steps wait for every load in flight.
+  for (; kt0 < KT; kt0 += NSTAGE) {
+    static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
+      const int64_t kt = kt0 + decltype(b)::value;
+      if (kt < KT) kstep(b, kt + 1 < KT, kt + NSTAGE < KT, std::integral_constant<int, 0>{});
+    });
+  }
+#else
   // One K step: wait for its stage, barrier, read the wave's fragments,
   // optionally issue the DMA of stage kt+NSTAGE-1, multiply.
   auto kstep = [&](auto b, int64_t kt, bool do_issue, auto waitn) __attribute__((always_inline)) {
@@ -573,6 +727,8 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
       if (kt < KT) kstep(b, kt, kt + NSTAGE - 1 < KT, std::integral_constant<int, 0>{});
     });
   }
+
+#endif
 
   tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds_epi, lane, wave, wave_m, wave_n, m0,
                                       SILU ? o0 : (int64_t)blockIdx.x * BN, m, n, out, epi);
