@@ -270,7 +270,6 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
-  const uint8_t* w_scales = w_packed + ntiles_total * kTileN * (KT * kTileK) / 2;
   const bool k_aligned64 = (k & 63) == 0;
   const int64_t o0 = SILU ? (int64_t)blockIdx.x * (BN / 2) : 0;
 
@@ -320,7 +319,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
       const int q = t + i * NT;
       const int tl = q >> 6, ln = q & 63;
       const bool ok = q < B_CHUNKS && tile_ok(tl);
-      rb[i] = ld16(w_packed + (ntile_of(tl) * KT + kt) * kTileCodeBytes + ln * 16, ok);
+      rb[i] = ld16(w_packed + (ntile_of(tl) * KT + kt) * kTileBytes + ln * 16, ok);
     }
 #pragma unroll
     for (int i = 0; i < BS_PER_T; ++i) {
@@ -328,7 +327,8 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
       const int tl = q >> 5, c = q & 31;
       uint32_t v = 0;
       if (q < BN && tile_ok(tl))
-        v = *reinterpret_cast<const uint32_t*>(w_scales + (ntile_of(tl) * KT + kt) * kTileScaleBytes + c * 4);
+        v = *reinterpret_cast<const uint32_t*>(w_packed + (ntile_of(tl) * KT + kt) * kTileBytes + kTileCodeBytes +
+                                               c * 4);
       rbs[i] = v;
     }
   };
@@ -494,7 +494,6 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const uint32_t a_row_bytes = (uint32_t)(k / 2), a_row_scales = (uint32_t)(k / 16);
-  const uint8_t* w_scales = w_packed + ntiles_total * kTileN * k / 2;
   const int64_t o0 = SILU ? (int64_t)blockIdx.x * (BN / 2) : 0;
 
   auto ntile_of = [&](int tl) -> int64_t {
@@ -529,12 +528,12 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
       dst[i] = P::OFF_AS + g * 256;
     } else if (i < I_BS) {
       const int tl = q - P::N_AC - P::N_AS;
-      src[i] = w_packed + ntile_of(tl) * KT * kTileCodeBytes + lane * 16;
+      src[i] = w_packed + ntile_of(tl) * KT * kTileBytes + lane * 16;
       dst[i] = P::OFF_BC + tl * 1024;
     } else {
       const int p = q - P::N_AC - P::N_AS - P::N_BC;
       const int tl = 2 * p + h;
-      src[i] = w_scales + ntile_of(tl) * KT * kTileScaleBytes + r * 4;
+      src[i] = w_packed + ntile_of(tl) * KT * kTileBytes + kTileCodeBytes + r * 4;
       dst[i] = P::OFF_BS + p * 256;
     }
   }
@@ -545,8 +544,8 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     for (int i = 0; i < P::LPW; ++i) {
       if (i < I_AS) { dma16(src[i], base + dst[i]); src[i] += 32; }
       else if (i < I_BC) { dma4(src[i], base + dst[i]); src[i] += 4; }
-      else if (i < I_BS) { dma16(src[i], base + dst[i]); src[i] += kTileCodeBytes; }
-      else { dma4(src[i], base + dst[i]); src[i] += kTileScaleBytes; }
+      else if (i < I_BS) { dma16(src[i], base + dst[i]); src[i] += kTileBytes; }
+      else { dma4(src[i], base + dst[i]); src[i] += kTileBytes; }
     }
   };
 
@@ -771,8 +770,6 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   const int lane = t & 63, r = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t KT = (k + kTileK - 1) / kTileK;
-  const int64_t np = (n + kTileN - 1) / kTileN * kTileN;
-  const uint8_t* w_scales = w_packed + np * (KT * kTileK) / 2;
   const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
   int64_t slab[NS];
   slab[0] = blockIdx.x;
@@ -817,8 +814,8 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int64_t tile = slab[j] * KT + kt;                      // wave-uniform
-      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile * kTileCodeBytes + w_lane);
-      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_scales + tile * kTileScaleBytes + ws_lane);
+      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile * kTileBytes + w_lane);
+      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_packed + tile * kTileBytes + kTileCodeBytes + ws_lane);
     }
   };
   auto compute = [&](int64_t kt, const Tile& T) __attribute__((always_inline)) {

@@ -141,15 +141,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // --------------------------------------------------- packed weight layout ----
 // Weights are stored in tiles of 32 rows (output features) x 64 columns (K).
-// Tile (nt, kt) holds 1024 code bytes in MFMA lane order -- lane l = c + 32*h
-// owns the 16 bytes of row c, columns 32h..32h+31 -- followed, in a separate
-// region after all codes, by 128 scale bytes: row c's four block scales at
-// c*4..c*4+3.  Tiles are ordered nt-major (a row of tiles along K is
-// contiguous), so a wave streams one 32-row slab with fully coalesced 16-byte
-// loads.
+// Tile (nt, kt) occupies kTileBytes = 1152 bytes: 1024 code bytes in MFMA lane
+// order -- lane l = c + 32*h owns the 16 bytes of row c, columns 32h..32h+31
+// -- then its 128 scale bytes, row c's four block scales at 1024 + c*4.
+// Tiles are ordered nt-major (a row of tiles along K is contiguous), so a wave
+// streams one 32-row slab with fully coalesced 16-byte loads and finds each
+// tile's scales right behind its codes.
 constexpr int kTileN = 32;
 constexpr int kTileK = 64;
 constexpr int kTileCodeBytes = kTileN * kTileK / 2;   // 1024
 constexpr int kTileScaleBytes = kTileN * kTileK / 16; // 128
+constexpr int kTileBytes = kTileCodeBytes + kTileScaleBytes;
 
 }  // namespace nvfp4

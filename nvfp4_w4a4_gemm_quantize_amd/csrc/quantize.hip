@@ -130,7 +130,6 @@ pack_kernel(const uint16_t* __restrict__ w, int64_t n, int64_t k, int64_t np, in
   const int64_t bpr = kp >> 4;
   const int64_t kt_count = kp / kTileK;
   const int64_t total = np * bpr;
-  uint8_t* scale_region = packed + np * kp / 2;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * kThreads) {
     const int64_t row = i / bpr, b = i % bpr;
@@ -145,8 +144,9 @@ pack_kernel(const uint16_t* __restrict__ w, int64_t n, int64_t k, int64_t np, in
     const int64_t kt = b >> 2, bin = b & 3;        // block within the 64-wide tile
     const int64_t tile = nt * kt_count + kt;
     const int64_t lane = cc + kTileN * (bin >> 1);
-    *reinterpret_cast<uint2*>(packed + tile * kTileCodeBytes + lane * 16 + (bin & 1) * 8) = c;
-    scale_region[tile * kTileScaleBytes + cc * 4 + bin] = (uint8_t)S;
+    uint8_t* t = packed + tile * kTileBytes;
+    *reinterpret_cast<uint2*>(t + lane * 16 + (bin & 1) * 8) = c;
+    t[kTileCodeBytes + cc * 4 + bin] = (uint8_t)S;
   }
 }
 
@@ -155,7 +155,6 @@ unpack_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int64_t 
               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int64_t bpr = k >> 4;
   const int64_t kt_count = kp / kTileK;
-  const uint8_t* scale_region = packed + np * kp / 2;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n * bpr;
        i += (int64_t)gridDim.x * kThreads) {
     const int64_t row = i / bpr, b = i % bpr;
@@ -163,9 +162,10 @@ unpack_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int64_t 
     const int64_t kt = b >> 2, bin = b & 3;
     const int64_t tile = nt * kt_count + kt;
     const int64_t lane = cc + kTileN * (bin >> 1);
+    const uint8_t* t = packed + tile * kTileBytes;
     *reinterpret_cast<uint2*>(codes + row * (k / 2) + b * 8) =
-        *reinterpret_cast<const uint2*>(packed + tile * kTileCodeBytes + lane * 16 + (bin & 1) * 8);
-    scales[row * bpr + b] = scale_region[tile * kTileScaleBytes + cc * 4 + bin];
+        *reinterpret_cast<const uint2*>(t + lane * 16 + (bin & 1) * 8);
+    scales[row * bpr + b] = t[kTileCodeBytes + cc * 4 + bin];
   }
 }
 

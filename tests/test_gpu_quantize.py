@@ -193,8 +193,9 @@ def test_pack_ragged_and_padding(gpu_lib, n, k):
     packed, _, _, _ = gpu_pack_unpack(gpu_lib, bits)
     np_, kp = -(-n // 32) * 32, -(-k // 64) * 64
     kt = kp // 64
-    codes = packed[:np_ * kp // 2].reshape(np_ // 32, kt, 2, 32, 16)     # [nt, kt, h, c, 16 bytes]
-    scales = packed[np_ * kp // 2:np_ * kp // 2 + np_ * kp // 16].reshape(np_ // 32, kt, 32, 4)
+    tiles = packed[:np_ * kp * 9 // 16].reshape(np_ // 32, kt, 1152)    # [nt, kt, 1024 codes + 128 scales]
+    codes = tiles[:, :, :1024].reshape(np_ // 32, kt, 2, 32, 16)       # [nt, kt, h, c, 16 bytes]
+    scales = tiles[:, :, 1024:].reshape(np_ // 32, kt, 32, 4)          # [nt, kt, c, block]
     rows = np.arange(np_).reshape(np_ // 32, 32)
     cols_block = np.arange(kp // 16).reshape(kt, 4)
     pad_row = rows >= n
