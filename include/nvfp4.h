@@ -108,7 +108,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
  * nvfp4_packed_weight_bytes -- bytes of the opaque packed weight buffer for
  * an [n, k] weight (k % 16 == 0); 0 for invalid sizes.  It is the NVFP4
  * storage (k/2 + k/16 bytes per row, i.e. 4.5 bits per weight) of the weight
- * padded to whole 32-row x 64-column tiles.
+ * padded to 32-row x 256-column blocks (zero codes and scales in the padding).
  */
 size_t nvfp4_packed_weight_bytes(int64_t n, int64_t k);
 
@@ -160,8 +160,10 @@ int nvfp4_unpack_weights_linear(const void* packed, int64_t n, int64_t k,
  *                      (out aligned to its element size).
  *   epilogue           NONE, or SILU_MUL: requires n % 64 == 0 and computes
  *                      out[:, j] = silu(y[:, j]) * y[:, j + n/2].
- * m <= 64 runs the weight-streaming decode kernel, larger m the tiled
- * prefill kernel; both give results within 1e-5 * sum_k |a*w| * alpha.
+ * m <= 64 runs a weight-streaming decode kernel (m <= 4 without an epilogue:
+ * the block-scaled FP4 MFMA on the raw codes with the E4M3 scales applied in
+ * FP32; otherwise exact dequantisation to f16 and the f16 MFMA), larger m the
+ * tiled prefill kernel; all give results within 1e-5 * sum_k |a*w| * alpha.
  */
 int gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t m,
               const void* w_packed, const float* w_global, int64_t n, int64_t k,

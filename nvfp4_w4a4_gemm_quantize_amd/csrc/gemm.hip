@@ -267,6 +267,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
   const int lane = t & 63, r = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), wave_m = wave / WN, wave_n = wave % WN;
   const int64_t KT = (k + kTileK - 1) / kTileK;
+  const int64_t KS = super_count(k);
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
@@ -319,7 +320,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
       const int q = t + i * NT;
       const int tl = q >> 6, ln = q & 63;
       const bool ok = q < B_CHUNKS && tile_ok(tl);
-      rb[i] = ld16(w_packed + (ntile_of(tl) * KT + kt) * kTileBytes + ln * 16, ok);
+      rb[i] = ld16(w_packed + tile_code_off(ntile_of(tl), kt, KS) + ln * 16, ok);
     }
 #pragma unroll
     for (int i = 0; i < BS_PER_T; ++i) {
@@ -327,8 +328,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
       const int tl = q >> 5, c = q & 31;
       uint32_t v = 0;
       if (q < BN && tile_ok(tl))
-        v = *reinterpret_cast<const uint32_t*>(w_packed + (ntile_of(tl) * KT + kt) * kTileBytes + kTileCodeBytes +
-                                               c * 4);
+        v = *reinterpret_cast<const uint32_t*>(w_packed + tile_scale_off(ntile_of(tl), kt, KS, c));
       rbs[i] = v;
     }
   };
@@ -491,6 +491,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave_m = wave / WN, wave_n = wave % WN;
   const int64_t KT = k / kTileK;
+  const int64_t KS = super_count(k);
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const uint32_t a_row_bytes = (uint32_t)(k / 2), a_row_scales = (uint32_t)(k / 16);
@@ -528,24 +529,30 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
       dst[i] = P::OFF_AS + g * 256;
     } else if (i < I_BS) {
       const int tl = q - P::N_AC - P::N_AS;
-      src[i] = w_packed + ntile_of(tl) * KT * kTileBytes + lane * 16;
+      src[i] = w_packed + tile_code_off(ntile_of(tl), 0, KS) + lane * 16;
       dst[i] = P::OFF_BC + tl * 1024;
     } else {
       const int p = q - P::N_AC - P::N_AS - P::N_BC;
       const int tl = 2 * p + h;
-      src[i] = w_packed + ntile_of(tl) * KT * kTileBytes + kTileCodeBytes + r * 4;
+      src[i] = w_packed + tile_scale_off(ntile_of(tl), 0, KS, r);
       dst[i] = P::OFF_BS + p * 256;
     }
   }
   // Stages are issued strictly in order, so each load keeps a running source
-  // pointer that advances by its per-stage stride after every issue.
-  auto issue = [&](uint8_t* base) __attribute__((always_inline)) {
+  // pointer that advances by its per-stage stride after every issue.  With
+  // four stages, the buffer of a stage is its tile's position T in the weight
+  // super-tile, which fixes the weight strides at compile time.
+  static_assert(NSTAGE == kSuperTiles, "one stage buffer per tile of a weight super-tile");
+  auto issue = [&](uint8_t* base, auto tpos) __attribute__((always_inline)) {
+    constexpr int T = decltype(tpos)::value;
+    constexpr int W_CODE_STEP = T < kSuperTiles - 1 ? kTileCodeBytes : kSuperBytes - (kSuperTiles - 1) * kTileCodeBytes;
+    constexpr int W_SCALE_STEP = T == 0 ? 4 : T == 1 ? kTileN * 8 - 4 : T == 2 ? 4 : kSuperBytes - kTileN * 8 - 4;
 #pragma unroll
     for (int i = 0; i < P::LPW; ++i) {
       if (i < I_AS) { dma16(src[i], base + dst[i]); src[i] += 32; }
       else if (i < I_BC) { dma4(src[i], base + dst[i]); src[i] += 4; }
-      else if (i < I_BS) { dma16(src[i], base + dst[i]); src[i] += kTileBytes; }
-      else { dma4(src[i], base + dst[i]); src[i] += kTileBytes; }
+      else if (i < I_BS) { dma16(src[i], base + dst[i]); src[i] += W_CODE_STEP; }
+      else { dma4(src[i], base + dst[i]); src[i] += W_SCALE_STEP; }
     }
   };
 
@@ -616,7 +623,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   half8_t oa0[MF], ob0[NF], oa1[MF], ob1[NF];
   // Prologue: all NSTAGE stages in flight (the launcher guarantees KT >= NSTAGE),
   // then stage 0 is read and its first sub-step dequantised.
-  static_for<0, NSTAGE>([&](auto s) __attribute__((always_inline)) { issue(buf(s)); });
+  static_for<0, NSTAGE>([&](auto s) __attribute__((always_inline)) { issue(buf(s), s); });
   sync_stage(std::integral_constant<int, P::LPW * (NSTAGE - 1)>{});
   read_frags(buf(std::integral_constant<int, 0>{}), R);
   dequant_step_h<MF, NF>(hsh, 0, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
@@ -653,7 +660,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     if (has_next) {
       sync_stage(waitn);
       read_frags(buf(std::integral_constant<int, (B + 1) % NSTAGE>{}), R);
-      if (do_issue) issue(buf(b));
+      if (do_issue) issue(buf(b), b);
       fence_sched();
       dequant_step_h<MF, NF>(hsh, 0, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
     }
@@ -703,12 +710,13 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
       bsc[j] = reinterpret_cast<const uint32_t*>(base + P::OFF_BS)[tl * 32 + r] >> (16 * h);
     }
     // The next stage's loads go out after this stage's reads are issued.
-    if (do_issue) issue(buf(std::integral_constant<int, (B + NSTAGE - 1) % NSTAGE>{}));
+    if (do_issue) issue(buf(std::integral_constant<int, (B + NSTAGE - 1) % NSTAGE>{}),
+                        std::integral_constant<int, (B + NSTAGE - 1) % NSTAGE>{});
     mma_k64<MF, NF>(acc, ac, asc, bc, bsc);
   };
 
   // Prologue: stages 0..NSTAGE-2 (the launcher guarantees KT >= NSTAGE).
-  static_for<0, NSTAGE - 1>([&](auto s) __attribute__((always_inline)) { issue(buf(s)); });
+  static_for<0, NSTAGE - 1>([&](auto s) __attribute__((always_inline)) { issue(buf(s), s); });
   // Steady state, in groups of NSTAGE steps with compile-time buffers; every
   // step issues, so the in-flight DMA pattern is the same at every step.
   int64_t kt0 = 0;
@@ -770,6 +778,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   const int lane = t & 63, r = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t KT = (k + kTileK - 1) / kTileK;
+  const int64_t KS = super_count(k);
   const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
   int64_t slab[NS];
   slab[0] = blockIdx.x;
@@ -790,7 +799,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
         for (int e = 0; e < 16; ++e) part[i][j][q][e] = 0.0f;
 
   // Per-lane constant offsets; per-tile bases are wave-uniform (scalar).
-  const uint32_t w_lane = lane * 16, ws_lane = r * 4 + 2 * h;
+  const uint32_t w_lane = lane * 16, ws_lane = r * 8 + 2 * h;
   // A in LDS (ALDS): 16-byte chunk (kt, s, hh, row) at ((kt*4 + s)*2 + hh)*(m+1) + row,
   // row m of every group is zero; lanes of rows >= m read it.
   const int64_t a_rows = m + 1;
@@ -812,10 +821,9 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
       }
     }
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int64_t tile = slab[j] * KT + kt;                      // wave-uniform
-      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile * kTileBytes + w_lane);
-      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_packed + tile * kTileBytes + kTileCodeBytes + ws_lane);
+    for (int j = 0; j < NS; ++j) {                                 // tile bases are wave-uniform
+      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile_code_off(slab[j], kt, KS) + w_lane);
+      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_packed + tile_scale_off(slab[j], kt, KS, 0) + ws_lane);
     }
   };
   auto compute = [&](int64_t kt, const Tile& T) __attribute__((always_inline)) {
@@ -945,6 +953,302 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   }
 }
 
+// ------------------------------------------------ decode kernel, FP4 MFMA ----
+// m <= 8: weight streaming on gfx950's block-scaled FP4 MFMA, applied to the
+// raw E2M1 codes (no dequantisation).  The packed weight tile is already the
+// B operand of v_mfma_scale_f32_32x32x64_f8f6f4 (lane r + 32h: column r, K
+// 32h..32h+31).  The A operand puts each 16-element block of each A row in a
+// row of its own -- MFMA row 4*mm + q holds row mm's block q of the tile and
+// zeros elsewhere -- so with unit E8M0 scales the 32x32 result holds the
+// per-block partial sums sum_{k in block q} a[mm][k] * w[n][k], exactly (the
+// products are multiples of 1/4 and a block sum stays far below 2^24).  Each
+// lane then applies the NVFP4 block scales in FP32:
+//   y[mm][n] += sum_q s_a[mm][q] * s_w[n][q] * C[4*mm + q][n].
+// Lane (r, h) holds rows mm = h, 2+h, ... of column r, so no cross-lane
+// reduction is needed; the K split across the workgroup's waves is summed in
+// LDS in a fixed order.  A is staged once per workgroup into LDS: one 16-byte
+// operand record per (tile, block, row) plus one zero record per tile (for
+// lanes whose MFMA row is empty), and the A block scales as FP32.
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+template <int MR>
+struct Fp4DecodeLds {
+  static constexpr int RECS = 4 * MR + 1;           // records per K tile (last: zeros)
+  __host__ __device__ static int64_t rec_bytes(int64_t kt_count) { return kt_count * RECS * 16; }
+  __host__ __device__ static int64_t scale_bytes(int64_t kt_count) { return (int64_t)MR * kt_count * 4 * 4; }
+};
+
+template <int MR, bool SILU, int DW, int SU>
+__global__ void __launch_bounds__(DW * 64) __attribute__((amdgpu_waves_per_eu(3)))
+gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
+                       const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
+                       EpilogueArgs epi) {
+  constexpr int NS = SILU ? 2 : 1;               // weight slabs per workgroup (gate, up)
+  constexpr int MH = MR / 2;                     // A rows per lane: h, 2+h, ...
+  using L = Fp4DecodeLds<MR>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, r = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t KS = super_count(k), KTP = KS * kSuperTiles;   // tiles incl. zero padding
+  const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
+  int64_t slab[NS];
+  slab[0] = blockIdx.x;
+  if (SILU) slab[NS - 1] = blockIdx.x + (n / 2) / kTileN;
+  // The waves split the slab's super-tiles (padding tiles hold zeros).
+  const int64_t ks0 = KS * wave / DW, ks1 = KS * (wave + 1) / DW;
+  const int64_t rec_total = L::rec_bytes(KTP) / 16;
+  float* s_sa = reinterpret_cast<float*>(smem + L::rec_bytes(KTP));
+
+  // One super-tile of each slab: four tiles of codes and, per lane, row r's
+  // scales for tiles 2h and 2h+1 (the other pair comes from lane r + 32(1-h)).
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  struct Super { uint4 b[NS][kSuperTiles]; uint2 bs[NS]; };
+  // Streaming loads (non-temporal: the weights are read once), unconditional
+  // and clamped to the wave's range so the compiler can count them.
+  auto load = [&](int64_t ks, Super& S) __attribute__((always_inline)) {
+    ks = ks < ks1 ? ks : ks1 - 1;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const uint8_t* sp = w_packed + (slab[j] * KS + ks) * kSuperBytes;   // wave-uniform
+#pragma unroll
+      for (int tt = 0; tt < kSuperTiles; ++tt) {
+        const u32x4_t cv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(sp + tt * kTileCodeBytes + lane * 16));
+        S.b[j][tt] = make_uint4(cv[0], cv[1], cv[2], cv[3]);
+      }
+      const u32x2_t sv = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sp + kSuperScaleOff + lane * 8));
+      S.bs[j] = make_uint2(sv[0], sv[1]);
+    }
+  };
+  Super g_a[SU], g_b[SU];
+  auto load_group = [&](int64_t g0, Super (&G)[SU]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < SU; ++u) load(g0 + u, G[u]);
+  };
+
+  // Stage A: operand records (one per (tile, block, row), plus a zero record
+  // per tile) and FP32 block scales.  When A is small (the usual decode case)
+  // a fixed, unrolled set of unconditional staging loads (invalid items read
+  // offset 0, which always exists, and are zeroed afterwards) is issued before
+  // the weight loads, so waiting for it does not wait for the weight stream.
+  constexpr int SPT = 4;
+  const uint32_t kt4 = (uint32_t)KTP * 4u, k32 = (uint32_t)k, m32 = (uint32_t)m;
+  const uint32_t nrec = (uint32_t)rec_total, nsc = (uint32_t)MR * kt4;
+  const bool fast_stage = nrec <= (uint32_t)(SPT * DW * 64) && nsc <= (uint32_t)(SPT * DW * 64);
+  auto rec_of = [&](uint32_t idx, bool& ok, bool& odd) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t kt = idx / L::RECS, rr = idx % L::RECS;
+    const uint32_t q = rr / MR, mm = rr % MR;
+    ok = idx < nrec && rr < 4 * MR && mm < m32 && kt * kTileK + q * 16 < k32;
+    odd = (q & 1) != 0;
+    return ok ? mm * (uint32_t)a_row_bytes + kt * 32 + q * 8 : 0u;
+  };
+  auto scale_of = [&](uint32_t idx, bool& ok) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t mm = idx / kt4, b = idx - mm * kt4;
+    ok = idx < nsc && mm < m32 && b * 16 < k32;
+    return ok ? mm * (uint32_t)a_row_scales + b : 0u;
+  };
+  auto record = [&](uint2 c, bool ok, bool odd) __attribute__((always_inline)) -> uint4 {
+    if (!ok) c = make_uint2(0u, 0u);
+    return odd ? make_uint4(0u, 0u, c.x, c.y) : make_uint4(c.x, c.y, 0u, 0u);
+  };
+  if (fast_stage) {
+    uint2 rc[SPT];
+    uint32_t sc[SPT];
+    bool rok[SPT], sok[SPT], rodd[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const uint32_t idx = (uint32_t)t + (uint32_t)(i * DW * 64);
+      rc[i] = *reinterpret_cast<const uint2*>(a_codes + rec_of(idx, rok[i], rodd[i]));
+      sc[i] = a_scales[scale_of(idx, sok[i])];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks0 < ks1) { load_group(ks0, g_a); load_group(ks0 + SU, g_b); }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const uint32_t idx = (uint32_t)t + (uint32_t)(i * DW * 64);
+      if (idx < nrec) *reinterpret_cast<uint4*>(smem + idx * 16) = record(rc[i], rok[i], rodd[i]);
+      if (idx < nsc) s_sa[idx] = sok[i] ? e4m3_decode(sc[i]) : 0.0f;
+    }
+  } else {
+    if (ks0 < ks1) { load_group(ks0, g_a); load_group(ks0 + SU, g_b); }
+    for (uint32_t idx = t; idx < nrec; idx += DW * 64) {
+      bool ok, odd;
+      const uint32_t off = rec_of(idx, ok, odd);
+      uint2 c = make_uint2(0u, 0u);
+      if (ok) c = *reinterpret_cast<const uint2*>(a_codes + off);
+      *reinterpret_cast<uint4*>(smem + idx * 16) = record(c, ok, odd);
+    }
+    for (uint32_t idx = t; idx < nsc; idx += DW * 64) {
+      bool ok;
+      const uint32_t off = scale_of(idx, ok);
+      s_sa[idx] = ok ? e4m3_decode(a_scales[off]) : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // This lane's A operand record within a tile: MFMA row r = 4*amm + aq.
+  const int amm = r >> 2, aq = r & 3;
+  const bool a_on = amm < MR && h == (aq >> 1);
+  const uint32_t a_lane = a_on ? (uint32_t)((aq * MR + amm) * 16) : (uint32_t)(4 * MR * 16);
+
+  // Partial sums per (slab, row[, block slot]): with one row per lane the four
+  // block slots get chains of their own, otherwise the rows are the chains.
+  constexpr int QC = MH == 1 ? 4 : 1;
+  float y4[NS][MH][QC];
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int i = 0; i < MH; ++i)
+#pragma unroll
+      for (int q = 0; q < QC; ++q) y4[j][i][q] = 0.0f;
+
+  // One tile: its MFMA results and the FP32 scale products s_a * s_w.
+  struct Prod { floatx16 c[NS]; float p[NS][MH][4]; };
+  auto tile_mfma = [&](int64_t kt, const uint4 (&wb)[NS], const uint32_t (&ws)[NS], Prod& P)
+      __attribute__((always_inline)) {
+    const uint4 a4 = *reinterpret_cast<const uint4*>(smem + kt * (L::RECS * 16) + a_lane);
+    const v8i_t av = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
+    float4 sa[MH];
+#pragma unroll
+    for (int i = 0; i < MH; ++i) sa[i] = *reinterpret_cast<const float4*>(s_sa + ((2 * i + h) * KTP + kt) * 4);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const v8i_t bv = {(int)wb[j].x, (int)wb[j].y, (int)wb[j].z, (int)wb[j].w, 0, 0, 0, 0};
+      const floatx16 zero = {};
+      P.c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, zero, 4, 4, 0, 127, 0, 127);
+      const float sw0 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 0);
+      const float sw1 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 1);
+      const float sw2 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 2);
+      const float sw3 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 3);
+#pragma unroll
+      for (int i = 0; i < MH; ++i) {
+        P.p[j][i][0] = sa[i].x * sw0;
+        P.p[j][i][1] = sa[i].y * sw1;
+        P.p[j][i][2] = sa[i].z * sw2;
+        P.p[j][i][3] = sa[i].w * sw3;
+      }
+    }
+  };
+  auto tile_accumulate = [&](const Prod& P) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < MH; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y4[j][i][q % QC] += P.p[j][i][q] * P.c[j][4 * i + q];
+  };
+  // One super-tile, branch-free: row r's scales for all four tiles (own pair
+  // plus the other half's), then tile u+1's MFMA issued before tile u's
+  // results are scaled and accumulated (with several rows or slabs per lane
+  // two tiles' state does not fit the register budget; those run in order).
+  auto compute_super = [&](int64_t ks, const Super& S) __attribute__((always_inline)) {
+    uint32_t ws[kSuperTiles][NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const uint32_t o0 = (uint32_t)__shfl_xor((int)S.bs[j].x, 32, 64);
+      const uint32_t o1 = (uint32_t)__shfl_xor((int)S.bs[j].y, 32, 64);
+      ws[0][j] = h == 0 ? S.bs[j].x : o0;
+      ws[1][j] = h == 0 ? S.bs[j].y : o1;
+      ws[2][j] = h == 0 ? o0 : S.bs[j].x;
+      ws[3][j] = h == 0 ? o1 : S.bs[j].y;
+    }
+    auto wb = [&](int tt, uint4 (&o)[NS]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) o[j] = S.b[j][tt];
+    };
+    const int64_t kt = ks * kSuperTiles;
+    if constexpr (NS * MH <= 2) {
+      Prod P[2];
+      uint4 b0[NS];
+      wb(0, b0);
+      tile_mfma(kt, b0, ws[0], P[0]);
+#pragma unroll
+      for (int u = 1; u < kSuperTiles; ++u) {
+        uint4 bu[NS];
+        wb(u, bu);
+        tile_mfma(kt + u, bu, ws[u], P[u & 1]);
+        tile_accumulate(P[(u - 1) & 1]);
+      }
+      tile_accumulate(P[(kSuperTiles - 1) & 1]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSuperTiles; ++u) {
+        uint4 bu[NS];
+        wb(u, bu);
+        Prod P1;
+        tile_mfma(kt + u, bu, ws[u], P1);
+        tile_accumulate(P1);
+      }
+    }
+  };
+  auto compute_group = [&](int64_t g0, const Super (&G)[SU]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+      if (g0 + u < ks1) compute_super(g0 + u, G[u]);
+  };
+  // Two groups of SU super-tiles in flight; each group is refilled after use.
+  if (ks0 < ks1) {
+    for (int64_t g = ks0; g < ks1; g += 2 * SU) {
+      compute_group(g, g_a);
+      if (g + 2 * SU < ks1) load_group(g + 2 * SU, g_a);
+      if (g + SU < ks1) compute_group(g + SU, g_b);
+      if (g + 3 * SU < ks1) load_group(g + 3 * SU, g_b);
+    }
+  }
+  float y[NS][MH];
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      float v = y4[j][i][0];
+#pragma unroll
+      for (int q = 1; q < QC; ++q) v += y4[j][i][q];
+      y[j][i] = v;
+    }
+
+  // Sum the waves' partial results in LDS (reusing the A staging area).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < MH; ++i) red[(((wave - 1) * NS + j) * MH + i) * 64 + lane] = y[j][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < DW - 1; ++w)
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < MH; ++i) y[j][i] += red[((w * NS + j) * MH + i) * 64 + lane];
+
+  const float ga = *epi.a_global;
+  const bool bf16 = epi.out_bf16 != 0;
+  const int64_t col = slab[0] * kTileN + r;
+  if (SILU) {
+    if (col >= n / 2) return;
+    const float alpha = 1.0f / (ga * epi.seg_w_global[0]);
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      const int64_t row = 2 * i + h;
+      if (row < m) store_out(out, bf16, row * epi.ld_out + col, silu_mul(y[0][i] * alpha, y[NS - 1][i] * alpha));
+    }
+  } else {
+    if (col >= n) return;
+    const ColumnEpilogue ce = column_epilogue(epi, col, ga);
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      const int64_t row = 2 * i + h;
+      if (row < m) store_out(out, bf16, row * epi.ld_out + col, apply_epilogue(ce, y[0][i]));
+    }
+  }
+}
+
 // ------------------------------------------------------------ launcher ----
 // Prefill tile: MF, NF (32x32 fragments per wave along M, N), WM, WN (waves), stages.
 #ifndef NVFP4_PREFILL_TILE
@@ -1003,8 +1307,44 @@ static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const
   }
 }
 
+// FP4-MFMA decode: LDS for the A records and scales (reused for the K-split
+// reduction); too large a K falls back to the f16 decode kernel.
+#ifndef NVFP4_DECODE_FP4_SU
+#define NVFP4_DECODE_FP4_SU 1
+#endif
+constexpr int kDecodeFp4Waves = 4;
+constexpr int64_t kDecodeFp4MaxLds = 56 * 1024;
+
+template <int MR, bool SILU>
+static bool launch_decode_fp4(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
+                              int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+  using L = Fp4DecodeLds<MR>;
+  constexpr int DW = kDecodeFp4Waves;
+  const int64_t ktp = super_count(k) * kSuperTiles;
+  const int64_t red = (int64_t)(DW - 1) * (SILU ? 2 : 1) * (MR / 2) * 64 * 4;
+  int64_t lds = L::rec_bytes(ktp) + L::scale_bytes(ktp);
+  if (lds < red) lds = red;
+  if (lds > kDecodeFp4MaxLds) return false;
+  const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
+  hipLaunchKernelGGL((gemm_decode_fp4_kernel<MR, SILU, DW, NVFP4_DECODE_FP4_SU>), dim3((unsigned)slabs),
+                     dim3(DW * 64), (unsigned)lds, st, ac, as, m, w, n, k, out, epi);
+  return true;
+}
+
+// The FP4 path covers plain (non-SILU) GEMMs with m <= 4: wider tiles of rows
+// or a second (gate/up) slab exceed its register budget, and those shapes run
+// no faster than the f16 decode kernel.
+static bool try_decode_fp4(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
+                           int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+  if (epi.silu_mul) return false;
+  if (m <= 2) return launch_decode_fp4<2, false>(ac, as, m, w, n, k, out, epi, st);
+  if (m <= 4) return launch_decode_fp4<4, false>(ac, as, m, w, n, k, out, epi, st);
+  return false;
+}
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+  if (m <= 4 && try_decode_fp4(a_codes, a_scales, m, w_packed, n, k, out, epi, st)) return hipGetLastError();
   if (m <= 64) {
     if (m <= 32) {
       if (epi.silu_mul) launch_decode<1, true>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);

@@ -140,17 +140,34 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // --------------------------------------------------- packed weight layout ----
-// Weights are stored in tiles of 32 rows (output features) x 64 columns (K).
-// Tile (nt, kt) occupies kTileBytes = 1152 bytes: 1024 code bytes in MFMA lane
-// order -- lane l = c + 32*h owns the 16 bytes of row c, columns 32h..32h+31
-// -- then its 128 scale bytes, row c's four block scales at 1024 + c*4.
-// Tiles are ordered nt-major (a row of tiles along K is contiguous), so a wave
-// streams one 32-row slab with fully coalesced 16-byte loads and finds each
-// tile's scales right behind its codes.
+// Weights are stored in tiles of 32 rows (output features) x 64 columns (K),
+// grouped four along K into super-tiles of 4608 bytes:
+//   bytes [t*1024, t*1024+1024): tile t's codes in MFMA lane order -- lane
+//     l = c + 32*h owns the 16 bytes of row c, columns 32h..32h+31;
+//   bytes [4096, 4608): the scales of the four tiles -- at 4096 + (g*32 + c)*8
+//     the eight bytes of row c for tiles 2g and 2g+1 (four block scales each).
+// A 32-row slab is a run of K/256 super-tiles (K padded to 256 with zero
+// codes and zero scales), so a wave streams it with coalesced 16-byte loads,
+// and one 8-byte load per lane (plus a swap across the wave halves) brings a
+// row's scales for four tiles.
 constexpr int kTileN = 32;
 constexpr int kTileK = 64;
 constexpr int kTileCodeBytes = kTileN * kTileK / 2;   // 1024
 constexpr int kTileScaleBytes = kTileN * kTileK / 16; // 128
-constexpr int kTileBytes = kTileCodeBytes + kTileScaleBytes;
+constexpr int kSuperTiles = 4;                        // tiles per super-tile along K
+constexpr int kSuperK = kSuperTiles * kTileK;         // 256
+constexpr int kSuperBytes = kSuperTiles * (kTileCodeBytes + kTileScaleBytes);   // 4608
+constexpr int kSuperScaleOff = kSuperTiles * kTileCodeBytes;                      // 4096
+
+// Number of super-tiles along K for a K dimension of k elements.
+__host__ __device__ inline int64_t super_count(int64_t k) { return (k + kSuperK - 1) / kSuperK; }
+// Byte offset of tile (nt, kt)'s codes; ks = super_count(k).
+__host__ __device__ inline int64_t tile_code_off(int64_t nt, int64_t kt, int64_t ks) {
+  return (nt * ks + (kt >> 2)) * kSuperBytes + (kt & 3) * kTileCodeBytes;
+}
+// Byte offset of row c's four block scales of tile (nt, kt).
+__host__ __device__ inline int64_t tile_scale_off(int64_t nt, int64_t kt, int64_t ks, int64_t c) {
+  return (nt * ks + (kt >> 2)) * kSuperBytes + kSuperScaleOff + (((kt & 3) >> 1) * kTileN + c) * 8 + (kt & 1) * 4;
+}
 
 }  // namespace nvfp4

@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(kThreads)
 pack_kernel(const uint16_t* __restrict__ w, int64_t n, int64_t k, int64_t np, int64_t kp,
             SegmentTable segs, const float* __restrict__ seg_g, uint8_t* __restrict__ packed) {
   const int64_t bpr = kp >> 4;
-  const int64_t kt_count = kp / kTileK;
+  const int64_t ks = kp / kSuperK;
   const int64_t total = np * bpr;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * kThreads) {
@@ -142,11 +142,9 @@ pack_kernel(const uint16_t* __restrict__ w, int64_t n, int64_t k, int64_t np, in
     }
     const int64_t nt = row / kTileN, cc = row % kTileN;
     const int64_t kt = b >> 2, bin = b & 3;        // block within the 64-wide tile
-    const int64_t tile = nt * kt_count + kt;
     const int64_t lane = cc + kTileN * (bin >> 1);
-    uint8_t* t = packed + tile * kTileBytes;
-    *reinterpret_cast<uint2*>(t + lane * 16 + (bin & 1) * 8) = c;
-    t[kTileCodeBytes + cc * 4 + bin] = (uint8_t)S;
+    *reinterpret_cast<uint2*>(packed + tile_code_off(nt, kt, ks) + lane * 16 + (bin & 1) * 8) = c;
+    packed[tile_scale_off(nt, kt, ks, cc) + bin] = (uint8_t)S;
   }
 }
 
@@ -154,18 +152,16 @@ __global__ void __launch_bounds__(kThreads)
 unpack_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int64_t np, int64_t kp,
               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int64_t bpr = k >> 4;
-  const int64_t kt_count = kp / kTileK;
+  const int64_t ks = kp / kSuperK;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n * bpr;
        i += (int64_t)gridDim.x * kThreads) {
     const int64_t row = i / bpr, b = i % bpr;
     const int64_t nt = row / kTileN, cc = row % kTileN;
     const int64_t kt = b >> 2, bin = b & 3;
-    const int64_t tile = nt * kt_count + kt;
     const int64_t lane = cc + kTileN * (bin >> 1);
-    const uint8_t* t = packed + tile * kTileBytes;
     *reinterpret_cast<uint2*>(codes + row * (k / 2) + b * 8) =
-        *reinterpret_cast<const uint2*>(t + lane * 16 + (bin & 1) * 8);
-    scales[row * bpr + b] = t[kTileCodeBytes + cc * 4 + bin];
+        *reinterpret_cast<const uint2*>(packed + tile_code_off(nt, kt, ks) + lane * 16 + (bin & 1) * 8);
+    scales[row * bpr + b] = packed[tile_scale_off(nt, kt, ks, cc) + bin];
   }
 }
 
@@ -207,7 +203,7 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_
 
 hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const SegmentTable& segs, float* seg_g,
                        bool dynamic, uint8_t* packed, hipStream_t st) {
-  const int64_t np = round_up(n, kTileN), kp = round_up(k, kTileK);
+  const int64_t np = round_up(n, kTileN), kp = round_up(k, kSuperK);
   if (dynamic) {
     // Partials in the packed buffer (>= 1152 bytes), overwritten by the pack.
     int64_t cap = (np * kp / 2) / 4 / segs.num;
@@ -224,7 +220,7 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const SegmentTab
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
                          hipStream_t st) {
-  const int64_t np = round_up(n, kTileN), kp = round_up(k, kTileK);
+  const int64_t np = round_up(n, kTileN), kp = round_up(k, kSuperK);
   hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(n * (k / 16), 16384)), dim3(kThreads), 0, st,
                      packed, n, k, np, kp, codes, scales);
   return hipGetLastError();

@@ -20,7 +20,7 @@ int validate_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, c
 
 size_t packed_weight_bytes(int64_t n, int64_t k) {
   if (n <= 0 || k <= 0 || k % 16 != 0) return 0;
-  const int64_t np = (n + 31) / 32 * 32, kp = (k + 63) / 64 * 64;
+  const int64_t np = (n + 31) / 32 * 32, kp = (k + 255) / 256 * 256;   // 32-row slabs, 256-wide super-tiles
   return (size_t)(np * kp / 2 + np * kp / 16);
 }
 

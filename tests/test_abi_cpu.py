@@ -59,7 +59,7 @@ def test_packed_weight_bytes(lib):
     f = lib.nvfp4_packed_weight_bytes
     assert f(17408, 5120) == 17408 * 5120 * 9 // 16          # 4.5 bits per weight, no padding
     assert f(16480, 5120) == 16480 * 5120 * 9 // 16
-    assert f(100, 80) == 128 * 128 * 9 // 16                 # padded to 32 x 64 tiles
+    assert f(100, 80) == 128 * 256 * 9 // 16                 # padded to 32-row slabs of 256-wide super-tiles
     assert f(0, 64) == 0 and f(64, 0) == 0 and f(64, 24) == 0 and f(-1, 64) == 0
 
 

@@ -191,11 +191,12 @@ def test_pack_ragged_and_padding(gpu_lib, n, k):
     check_pack(gpu_lib, bits, what="%dx%d" % (n, k))
     # padding rows/columns of the tiles hold zero codes and zero scales
     packed, _, _, _ = gpu_pack_unpack(gpu_lib, bits)
-    np_, kp = -(-n // 32) * 32, -(-k // 64) * 64
+    np_, kp = -(-n // 32) * 32, -(-k // 256) * 256
     kt = kp // 64
-    tiles = packed[:np_ * kp * 9 // 16].reshape(np_ // 32, kt, 1152)    # [nt, kt, 1024 codes + 128 scales]
-    codes = tiles[:, :, :1024].reshape(np_ // 32, kt, 2, 32, 16)       # [nt, kt, h, c, 16 bytes]
-    scales = tiles[:, :, 1024:].reshape(np_ // 32, kt, 32, 4)          # [nt, kt, c, block]
+    sup = packed[:np_ * kp * 9 // 16].reshape(np_ // 32, kp // 256, 4608)   # [nt, super-tile, 4 x 1024 codes + 512]
+    codes = sup[:, :, :4096].reshape(np_ // 32, kt, 2, 32, 16)             # [nt, kt, h, c, 16 bytes]
+    scales = sup[:, :, 4096:].reshape(np_ // 32, kp // 256, 2, 32, 2, 4)   # [nt, s, g, c, tile 2g+i, block]
+    scales = scales.transpose(0, 1, 2, 4, 3, 5).reshape(np_ // 32, kt, 32, 4)  # [nt, kt, c, block]
     rows = np.arange(np_).reshape(np_ // 32, 32)
     cols_block = np.arange(kp // 16).reshape(kt, 4)
     pad_row = rows >= n
