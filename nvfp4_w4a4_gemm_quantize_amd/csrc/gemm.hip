@@ -410,11 +410,43 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
 // relies on it) and only feeds output rows/columns that are never stored.
 // Loads for stage kt+NSTAGE-1 are issued right after the barrier of step kt,
 // into the buffer step kt-1 has finished with.
-// VALU ops issued after each MFMA in the pipelined main loop (0: the
-// unpipelined loop).
+// VALU ops issued after each MFMA in the pipelined main loop, and the MFMAs
+// of the last sub-step issued before any VALU op that needs the next stage.
 #ifndef NVFP4_XPIPE
 #define NVFP4_XPIPE 5
 #endif
+#ifndef NVFP4_LATE
+#define NVFP4_LATE 3
+#endif
+
+// Which output tile a workgroup of the prefill kernel computes (1-D grids).
+// sub == 0: tile first + blockIdx.x of a row-major grid gx tiles wide.
+// sub == 1: the workgroup's tile is half as tall; two workgroups cover each
+//           tile first + blockIdx.x / 2 of the gx-wide grid of full tiles.
+// sub == 2: the workgroup's tile is half as tall and half as wide; four
+//           workgroups cover each tile first + blockIdx.x / 4.
+// (sub > 0 serves the last, partly filled round of a launch.)
+struct TileMap {
+  int gx;
+  int first;
+  int sub;
+};
+
+__device__ __forceinline__ void map_tile(const TileMap& tm, int& bx, int& by) {
+  if (tm.sub == 0) {
+    const int t = tm.first + (int)blockIdx.x;
+    bx = t % tm.gx;
+    by = t / tm.gx;
+  } else if (tm.sub == 1) {
+    const int t = tm.first + (int)(blockIdx.x >> 1), q = (int)(blockIdx.x & 1);
+    bx = t % tm.gx;
+    by = (t / tm.gx) * 2 + q;
+  } else {
+    const int t = tm.first + (int)(blockIdx.x >> 2), q = (int)(blockIdx.x & 3);
+    bx = (t % tm.gx) * 2 + (q & 1);
+    by = (t / tm.gx) * 2 + (q >> 1);
+  }
+}
 
 template <int MF, int NF, int WM, int WN, int NSTAGE>
 struct DmaShape {
@@ -427,12 +459,17 @@ struct DmaShape {
   static constexpr int OFF_BC = OFF_AS + BM * 4;
   static constexpr int OFF_BS = OFF_BC + NTILES * 1024;
   static constexpr int STAGE = OFF_BS + NTILES * 128;
+  // Load classes: A code fragments, A scale groups (64 rows), W tiles, W scale
+  // pairs (two tiles).  Each wave issues the same number of DMA instructions
+  // per class; where a class does not split evenly, the surplus issues repeat
+  // an item (same source, same destination, same bytes), which keeps every
+  // wave's vmcnt accounting identical.
   static constexpr int N_AC = AFRAGS, N_AS = BM / 64, N_BC = NTILES, N_BS = NTILES / 2;
-  static constexpr int LOADS = N_AC + N_AS + N_BC + N_BS;
-  static constexpr int LPW = LOADS / NWAVES;            // DMA instructions per wave per stage
+  static constexpr int PC_AC = (N_AC + NWAVES - 1) / NWAVES, PC_AS = (N_AS + NWAVES - 1) / NWAVES;
+  static constexpr int PC_BC = (N_BC + NWAVES - 1) / NWAVES, PC_BS = (N_BS + NWAVES - 1) / NWAVES;
+  static constexpr int LPW = PC_AC + PC_AS + PC_BC + PC_BS;   // DMA instructions per wave per stage
   static constexpr int EPI_BYTES = NWAVES * 32 * 33 * 4;
-  static_assert(N_AC % NWAVES == 0 && N_AS % NWAVES == 0 && N_BC % NWAVES == 0 && N_BS % NWAVES == 0,
-                "each load class must split evenly over the waves");
+  static_assert(BM % 64 == 0 && NTILES % 2 == 0, "A scales move in 64-row groups, W scales in tile pairs");
 };
 
 // Global -> LDS DMA of 16 (or 4) bytes per lane: lane l's bytes land at
@@ -460,11 +497,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU>
+template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU, bool PIPE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
                         const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
-                        EpilogueArgs epi) {
+                        EpilogueArgs epi, TileMap tmap) {
   using P = DmaShape<MF, NF, WM, WN, NSTAGE>;
   constexpr int NWAVES = P::NWAVES, BM = P::BM, BN = P::BN, NTILES = P::NTILES;
   static_assert(NSTAGE == 3 || NSTAGE == 4, "3 or 4 stages");
@@ -493,9 +530,11 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   const int64_t KT = k / kTileK;
   const int64_t KS = super_count(k);
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  int bx, by;
+  map_tile(tmap, bx, by);
+  const int64_t m0 = (int64_t)by * BM;
   const uint32_t a_row_bytes = (uint32_t)(k / 2), a_row_scales = (uint32_t)(k / 16);
-  const int64_t o0 = SILU ? (int64_t)blockIdx.x * (BN / 2) : 0;
+  const int64_t o0 = SILU ? (int64_t)bx * (BN / 2) : 0;
 
   auto ntile_of = [&](int tl) -> int64_t {
     int64_t nt;
@@ -503,7 +542,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
       const int half = NTILES / 2;
       nt = tl < half ? (o0 / 32 + tl) : ((n / 2 + o0) / 32 + (tl - half));
     } else {
-      nt = (int64_t)blockIdx.x * NTILES + tl;
+      nt = (int64_t)bx * NTILES + tl;
     }
     return nt < ntiles_total ? nt : ntiles_total - 1;   // clamped: see the kernel comment
   };
@@ -513,26 +552,25 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   // Load classes in order: A code fragments, A scale groups (64 rows), W tiles,
   // W scale pairs; class sizes are multiples of the wave count, so load i of
   // every wave belongs to the same class (known at compile time).
-  constexpr int I_AS = P::N_AC / NWAVES, I_BC = I_AS + P::N_AS / NWAVES, I_BS = I_BC + P::N_BC / NWAVES;
+  constexpr int I_AS = P::PC_AC, I_BC = I_AS + P::PC_AS, I_BS = I_BC + P::PC_BC;
   const uint8_t* src[P::LPW];
   int dst[P::LPW];
 #pragma unroll
   for (int i = 0; i < P::LPW; ++i) {
-    const int q = wave + i * NWAVES;
     if (i < I_AS) {
-      const int f = q;
+      const int f = (wave + i * NWAVES) % P::N_AC;
       src[i] = a_codes + row_of(m0 + 32 * f + r) * a_row_bytes + h * 16;
       dst[i] = f * 1024;
     } else if (i < I_BC) {
-      const int g = q - P::N_AC;
+      const int g = (wave + (i - I_AS) * NWAVES) % P::N_AS;
       src[i] = a_scales + row_of(m0 + 64 * g + lane) * a_row_scales;
       dst[i] = P::OFF_AS + g * 256;
     } else if (i < I_BS) {
-      const int tl = q - P::N_AC - P::N_AS;
+      const int tl = (wave + (i - I_BC) * NWAVES) % P::N_BC;
       src[i] = w_packed + tile_code_off(ntile_of(tl), 0, KS) + lane * 16;
       dst[i] = P::OFF_BC + tl * 1024;
     } else {
-      const int p = q - P::N_AC - P::N_AS - P::N_BC;
+      const int p = (wave + (i - I_BS) * NWAVES) % P::N_BS;
       const int tl = 2 * p + h;
       src[i] = w_packed + tile_scale_off(ntile_of(tl), 0, KS, r);
       dst[i] = P::OFF_BS + p * 256;
@@ -569,10 +607,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     return wave_n * NF + j;
   };
 
-#if NVFP4_XPIPE > 0
-#ifndef NVFP4_LATE
-#define NVFP4_LATE 3
-#endif
+if constexpr (PIPE) {
   // Software pipeline across K steps.  Within step kt the four 16-wide
   // sub-steps multiply operands that were dequantised during the previous
   // sub-step, so the VALU work issues in the MFMA shadow.  Between sub-steps
@@ -682,7 +717,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
       if (kt < KT) kstep(b, kt + 1 < KT, kt + NSTAGE < KT, std::integral_constant<int, 0>{});
     });
   }
-#else
+} else {
   // One K step: wait for its stage, barrier, read the wave's fragments,
   // optionally issue the DMA of stage kt+NSTAGE-1, multiply.
   auto kstep = [&](auto b, int64_t kt, bool do_issue, auto waitn) __attribute__((always_inline)) {
@@ -735,10 +770,10 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     });
   }
 
-#endif
+}
 
   tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds_epi, lane, wave, wave_m, wave_n, m0,
-                                      SILU ? o0 : (int64_t)blockIdx.x * BN, m, n, out, epi);
+                                      SILU ? o0 : (int64_t)bx * BN, m, n, out, epi);
 }
 
 // ------------------------------------------------------- decode kernel ----
@@ -1258,6 +1293,19 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
 #define NVFP4_PREFILL_STAGES 4
 #endif
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
 template <int MF, int NF, int WM, int WN>
 static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
                            int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
@@ -1268,10 +1316,37 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
   dim3 grid((unsigned)((cols + bn - 1) / bn), (unsigned)((m + BM - 1) / BM));
   dim3 block(WM * WN * 64);
   if ((k & 63) == 0 && k / kTileK >= NS) {
-    if (epi.silu_mul)
-      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, true>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
-    else
-      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, false>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
+    // One workgroup per CU at a time: when the last round would leave most
+    // CUs idle, its tiles run as a second launch of quarter-size (four per
+    // tile) or half-height (two per tile) workgroups -- whichever still fits
+    // one round -- which fills the machine and finishes that round sooner.
+    // (SiLU*mul tiles are only halved: a quarter would split gate from up.)
+    const int64_t tiles = (int64_t)grid.x * grid.y, cus = cu_count(), rem = tiles % cus;
+    int split = 0;
+    if (tiles > cus && rem > 0) {
+      if (!epi.silu_mul && rem * 4 <= cus) split = 2;
+      else if (rem * 2 <= cus) split = 1;
+    }
+    const int64_t nbig = split ? tiles - rem : tiles;
+    const TileMap big{(int)grid.x, 0, 0};
+    const TileMap tail{(int)grid.x, (int)nbig, split};
+    const dim3 tail_grid((unsigned)(rem * (split == 2 ? 4 : 2)));
+    if (epi.silu_mul) {
+      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, true, true>), dim3((unsigned)nbig), block, 0, st,
+                         ac, as, m, w, n, k, out, epi, big);
+      if (split == 1)
+        hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF / 2, NF, WM, WN, NS, true, true>), tail_grid, block, 0, st,
+                           ac, as, m, w, n, k, out, epi, tail);
+    } else {
+      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, false, true>), dim3((unsigned)nbig), block, 0,
+                         st, ac, as, m, w, n, k, out, epi, big);
+      if (split == 1)
+        hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF / 2, NF, WM, WN, NS, false, true>), tail_grid, block, 0, st,
+                           ac, as, m, w, n, k, out, epi, tail);
+      if (split == 2)
+        hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF / 2, NF / 2, WM, WN, NS, false, true>), tail_grid, block, 0,
+                           st, ac, as, m, w, n, k, out, epi, tail);
+    }
   } else {
     if (epi.silu_mul)
       hipLaunchKernelGGL((gemm_prefill_regs_kernel<MF, NF, WM, WN, true>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);

@@ -74,6 +74,8 @@ def test_unit_scales_give_the_exact_integer_product(gpu_lib):
     (37, 96, 5120, "f32"),       # decode kernel, long K
     (1, 33, 32, "f32"),          # smallest K
     (512, 256, 1024, "bf16"),
+    (512, 33184, 256, "bf16"),   # 260 tiles of 256x256: on 256 CUs the last 4 run as quarter tiles; ragged N
+    (512, 46040, 256, "f32"),    # 360 tiles: the last 104 run as half-height tiles; ragged N
 ])
 def test_gemm_matches_oracle_everywhere(gpu_lib, M, N, K, out):
     rng = np.random.default_rng(M * 1000003 + N * 101 + K)
@@ -244,10 +246,10 @@ def test_fused_segments_small(gpu_lib, M):
     assert_within(gpu_out_f64(y), ref, tol, "fused segments M=%d" % M)
 
 
-@pytest.mark.parametrize("M", [1, 40, 130])
-def test_silu_mul_small(gpu_lib, M):
+@pytest.mark.parametrize("M,K,N", [(1, 192, 256), (40, 192, 256), (130, 192, 256),
+                                   (512, 256, 38400)])   # 300 gate/up tiles: the last 44 run as half tiles
+def test_silu_mul_small(gpu_lib, M, K, N):
     rng = np.random.default_rng(100 + M)
-    K, N = 192, 256
     a = rng.standard_t(4, size=(M, K)).astype(np.float32)
     w = (rng.standard_normal((N, K)) / 8).astype(np.float32)
     a_bits, w_bits = inputs.f32_to_bf16_bits(a), inputs.f32_to_bf16_bits(w)
