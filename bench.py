@@ -253,7 +253,7 @@ def kernel_source_sha256():
 
 
 def measured_traffic():
-    """HBM bytes per prefill GEMM launch from the committed FETCH_SIZE/WRITE_SIZE summary (copy-calibrated),
+    """HBM bytes per prefill GEMM from the committed FETCH_SIZE/WRITE_SIZE summary (copy-calibrated),
     or None when it is missing or was taken on a different kernel source."""
     path = os.path.join(ROOT, TRAFFIC_PROFILE)
     if not os.path.exists(path):
@@ -337,11 +337,12 @@ def main():
                    "prefill_tokens": 4096, "decode_tokens": 1, "weights": "NVFP4 packed, 16-element E4M3 scales",
                    "activations": "quantized per call (dynamic FP32 global scale)"},
         "roofline": {"bound": "mfma",
-                     "kernel": "gemm_prefill_dma_kernel (3 launches per step: gdn, gate_up, down)",
+                     "kernel": "gemm_prefill_dma_kernel (3 GEMMs per step: gdn, gate_up, down; each a full-round "
+                               "launch plus a tail launch)",
                      "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": None if traffic is None else int(sum(traffic.values()) / 3),
-                     "traffic_per": "HBM bytes per launch (mean of the 3), FETCH_SIZE + WRITE_SIZE, copy-calibrated",
+                     "traffic_per": "HBM bytes per GEMM (mean of the 3), FETCH_SIZE + WRITE_SIZE, copy-calibrated",
                      "algorithmic_bytes": int(sum(ALGO_BYTES.values()) / 3),
                      "fp4_peak_frac_context": round(achieved / PEAK_FP4_TFLOPS, 4)},
         "prefill_ms": {k: round(dur[k], 4) for k in ("prefill", "gdn", "gate_up", "down")},
