@@ -201,6 +201,40 @@ __device__ __forceinline__ void dequant_step_h(uint32_t hsh, int s, const uint4 
   }
 }
 
+// The lane's two scale pairs (blocks 2h and 2h+1 of a 64-wide K tile) of each
+// fragment as f16 pairs, computed once per K step: sub-steps 0, 1 use pair 0
+// and sub-steps 2, 3 pair 1.
+template <int MF, int NF>
+__device__ __forceinline__ void scale_pairs(uint32_t hsh, const uint32_t (&asc)[MF], const uint32_t (&bsc)[NF],
+                                            half2_t (&sa)[MF][2], half2_t (&sb)[NF][2]) {
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    sa[i][0] = scale_pair_f16(__builtin_amdgcn_ubfe(asc[i], hsh, 8));
+    sa[i][1] = scale_pair_f16(__builtin_amdgcn_ubfe(asc[i], hsh + 8u, 8));
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    sb[j][0] = scale_pair_f16(__builtin_amdgcn_ubfe(bsc[j], hsh, 8));
+    sb[j][1] = scale_pair_f16(__builtin_amdgcn_ubfe(bsc[j], hsh + 8u, 8));
+  }
+}
+
+template <int MF, int NF>
+__device__ __forceinline__ void dequant_step_p(int s, const uint4 (&ac)[MF], const uint4 (&bc)[NF],
+                                               const half2_t (&sa)[MF][2], const half2_t (&sb)[NF][2],
+                                               half8_t (&av)[MF], half8_t (&bv)[NF]) {
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const uint32_t cw = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
+    av[i] = dequant8(cw, sa[i][s >> 1]);
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const uint32_t cw = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
+    bv[j] = dequant8(cw, sb[j][s >> 1]);
+  }
+}
+
 template <int MF, int NF>
 __device__ __forceinline__ void mma_k64(floatx16 (&acc)[MF][NF], const uint4 (&ac)[MF], const uint32_t (&asc)[MF],
                                         const uint4 (&bc)[NF], const uint32_t (&bsc)[NF]) {
@@ -656,12 +690,14 @@ if constexpr (PIPE) {
 
   Raw R;
   half8_t oa0[MF], ob0[NF], oa1[MF], ob1[NF];
+  half2_t spa[MF][2], spb[NF][2];
   // Prologue: all NSTAGE stages in flight (the launcher guarantees KT >= NSTAGE),
   // then stage 0 is read and its first sub-step dequantised.
   static_for<0, NSTAGE>([&](auto s) __attribute__((always_inline)) { issue(buf(s), s); });
   sync_stage(std::integral_constant<int, P::LPW * (NSTAGE - 1)>{});
   read_frags(buf(std::integral_constant<int, 0>{}), R);
-  dequant_step_h<MF, NF>(hsh, 0, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
+  scale_pairs<MF, NF>(hsh, R.asc, R.bsc, spa, spb);
+  dequant_step_p<MF, NF>(0, R.ac, R.bc, spa, spb, oa0, ob0);
 
   // Sub-step 3 follows the LDS reads of the next stage: its first MFMAs go out
   // before any VALU op that needs the new fragments.
@@ -679,15 +715,15 @@ if constexpr (PIPE) {
   auto kstep = [&](auto b, bool has_next, bool do_issue, auto waitn) __attribute__((always_inline)) {
     constexpr int B = decltype(b)::value;
     fence_sched();
-    dequant_step_h<MF, NF>(hsh, 1, R.ac, R.asc, R.bc, R.bsc, oa1, ob1);
+    dequant_step_p<MF, NF>(1, R.ac, R.bc, spa, spb, oa1, ob1);
     mma(oa0, ob0);
     interleave();
     fence_sched();
-    dequant_step_h<MF, NF>(hsh, 2, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
+    dequant_step_p<MF, NF>(2, R.ac, R.bc, spa, spb, oa0, ob0);
     mma(oa1, ob1);
     interleave();
     fence_sched();
-    dequant_step_h<MF, NF>(hsh, 3, R.ac, R.asc, R.bc, R.bsc, oa1, ob1);
+    dequant_step_p<MF, NF>(3, R.ac, R.bc, spa, spb, oa1, ob1);
     mma(oa0, ob0);
     interleave();
     fence_sched();
@@ -697,7 +733,8 @@ if constexpr (PIPE) {
       read_frags(buf(std::integral_constant<int, (B + 1) % NSTAGE>{}), R);
       if (do_issue) issue(buf(b), b);
       fence_sched();
-      dequant_step_h<MF, NF>(hsh, 0, R.ac, R.asc, R.bc, R.bsc, oa0, ob0);
+      scale_pairs<MF, NF>(hsh, R.asc, R.bsc, spa, spb);
+      dequant_step_p<MF, NF>(0, R.ac, R.bc, spa, spb, oa0, ob0);
     }
     mma(oa1, ob1);
     interleave_late();
