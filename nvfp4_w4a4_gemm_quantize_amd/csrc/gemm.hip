@@ -45,6 +45,21 @@ __device__ __forceinline__ ColumnEpilogue column_epilogue(const EpilogueArgs& e,
   return c;
 }
 
+// Per-column epilogue parameters of a workgroup's BN output columns
+// (col_base ...), written to LDS once per workgroup before its main loop so
+// the epilogue reads one LDS entry per column instead of searching the
+// segment table and dividing for every output.  Columns past n repeat the
+// last column (their outputs are never stored).
+template <int BN, int NT>
+__device__ __forceinline__ void fill_column_table(ColumnEpilogue* tab, const EpilogueArgs& e, int64_t col_base,
+                                                  int64_t n) {
+  const float ga = *e.a_global;
+  for (int c = (int)threadIdx.x; c < BN; c += NT) {
+    const int64_t col = col_base + c;
+    tab[c] = column_epilogue(e, col < n ? col : n - 1, ga);
+  }
+}
+
 __device__ __forceinline__ float apply_epilogue(const ColumnEpilogue& c, float acc) {
   float y = acc * c.alpha;
   if (c.type == 1) {
@@ -57,7 +72,22 @@ __device__ __forceinline__ float apply_epilogue(const ColumnEpilogue& c, float a
   return y;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// silu(g)*u = g*u / (1 + e^-g), with e^-g = 2^(-g*log2 e) on the hardware exp2
+// and the division as the hardware reciprocal (each within about an ulp of
+// fp32, far below the bf16 rounding of the result; e^-g = inf gives 0).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// The epilogue's LDS staging region belongs to one wave, and a wave's LDS
+// instructions execute in issue order, so only the compiler has to keep the
+// region's writes and reads in program order: no workgroup barrier.
+__device__ __forceinline__ void wave_lds_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ void store_out(void* out, bool bf16, int64_t idx, float v) {
   if (bf16) reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(v);
@@ -82,10 +112,12 @@ __device__ __forceinline__ uint32_t scale_byte(uint32_t pair, int s) { return (p
 // picked by compile-time cases, so the accumulators stay in registers.
 // col_base: first output column of the workgroup; wave_n's fragment jj covers
 // output columns col_base + (wave_n * NJ + jj) * 32 .. +31.
+// ctab: the workgroup's per-column table (fill_column_table; unused for SiLU*mul).
 template <int MF, int NF, int WM, int WN, bool SILU>
-__device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* lds, int lane, int wave,
-                                              int wave_m, int wave_n, int64_t m0, int64_t col_base,
-                                              int64_t m, int64_t n, void* out, const EpilogueArgs& epi) {
+__device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* lds, const ColumnEpilogue* ctab,
+                                              int lane, int wave, int wave_m, int wave_n, int64_t m0,
+                                              int64_t col_base, int64_t m, int64_t n, void* out,
+                                              const EpilogueArgs& epi) {
   constexpr int EPI_STRIDE = 33;
   constexpr int NJ = SILU ? NF / 2 : NF;
   const int r = lane & 31, h = lane >> 5;
@@ -128,23 +160,24 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
   const float alpha_silu = SILU ? 1.0f / (ga * epi.seg_w_global[0]) : 0.0f;
   for (int f = 0; f < NJ * MF; ++f) {
     const int jj = f / MF, i = f % MF;
-    const int64_t col0 = col_base + (int64_t)(wave_n * NJ + jj) * 32 + ec;
+    const int c0 = (wave_n * NJ + jj) * 32 + ec;
+    const int64_t col0 = col_base + c0;
     float v[4][4];
-    __syncthreads();
+    wave_lds_order();
     static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
       constexpr int F = decltype(c)::value;
       if (f == F) stage_frag(acc[F % MF][F / MF]);
     });
-    __syncthreads();
+    wave_lds_order();
     read_frag(v);
     if constexpr (SILU) {
       float u[4][4];
-      __syncthreads();
+      wave_lds_order();
       static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
         constexpr int F = decltype(c)::value;
         if (f == F) stage_frag(acc[F % MF][F / MF + NF / 2]);
       });
-      __syncthreads();
+      wave_lds_order();
       read_frag(u);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -153,7 +186,7 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
     } else {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const ColumnEpilogue ce = column_epilogue(epi, col0 + b < n ? col0 + b : n - 1, ga);
+        const ColumnEpilogue ce = ctab[c0 + b];
 #pragma unroll
         for (int a = 0; a < 4; ++a) v[a][b] = apply_epilogue(ce, v[a][b]);
       }
@@ -296,6 +329,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
   constexpr int BS_PER_T = (BN + NT - 1) / NT;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[P::LDS];
+  __shared__ ColumnEpilogue ctab[SILU ? 1 : P::BN];
 
   const int t = threadIdx.x;
   const int lane = t & 63, r = lane & 31, h = lane >> 5;
@@ -307,6 +341,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
   const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
   const bool k_aligned64 = (k & 63) == 0;
   const int64_t o0 = SILU ? (int64_t)blockIdx.x * (BN / 2) : 0;
+  if constexpr (!SILU) fill_column_table<BN, NT>(ctab, epi, (int64_t)blockIdx.x * BN, n);
 
   auto ntile_of = [&](int tl) -> int64_t {
     if (SILU) {
@@ -429,7 +464,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
     __syncthreads();
   }
 
-  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds, lane, wave, wave_m, wave_n, m0,
+  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds, ctab, lane, wave, wave_m, wave_n, m0,
                                       SILU ? o0 : (int64_t)blockIdx.x * BN, m, n, out, epi);
 }
 
@@ -550,6 +585,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[P::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[NSTAGE > 3 ? P::STAGE : 16];
   __shared__ __attribute__((aligned(16))) uint8_t lds_epi[P::EPI_BYTES];
+  __shared__ ColumnEpilogue ctab[SILU ? 1 : BN];
   auto buf = [&](auto b) __attribute__((always_inline)) -> uint8_t* {
     constexpr int B = decltype(b)::value;
     if constexpr (B == 0) return lds_s0 + 1024;
@@ -569,6 +605,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   const int64_t m0 = (int64_t)by * BM;
   const uint32_t a_row_bytes = (uint32_t)(k / 2), a_row_scales = (uint32_t)(k / 16);
   const int64_t o0 = SILU ? (int64_t)bx * (BN / 2) : 0;
+  if constexpr (!SILU) fill_column_table<BN, NWAVES * 64>(ctab, epi, (int64_t)bx * BN, n);
 
   auto ntile_of = [&](int tl) -> int64_t {
     int64_t nt;
@@ -809,7 +846,7 @@ if constexpr (PIPE) {
 
 }
 
-  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds_epi, lane, wave, wave_m, wave_n, m0,
+  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds_epi, ctab, lane, wave, wave_m, wave_n, m0,
                                       SILU ? o0 : (int64_t)bx * BN, m, n, out, epi);
 }
 
