@@ -192,6 +192,34 @@ int gemm_w4a4_fused_segments(const uint8_t* a_codes, const uint8_t* a_scales, co
                              const int* seg_epilogue, const float* a_log, const float* dt_bias,
                              void* out, int out_dtype, int64_t ld_out, nvfp4_stream_t stream);
 
+/*
+ * gemm_w4a4_silu_mul_quantize -- the MLP gate/up projection whose activation
+ * h = silu(gate) * up leaves the GEMM already quantised to NVFP4, as the A
+ * operand of the down projection: the 4-bit activations of W4A4
+ * (bayesiansapien page, TL;DR) produced in the epilogue, so h never goes
+ * through HBM in bf16.  The global scale of h is static: a calibrated value
+ * (h's amax is not known until the whole GEMM has finished).
+ *
+ * Each h[i][j] (j < n/2) is computed as by gemm_w4a4 with SILU_MUL from the
+ * tiled kernel, rounded to bf16, and that bf16 row is quantised exactly as
+ * nvfp4_quantize quantises a bf16 tensor with dynamic_global = 0 and global
+ * scale *h_global (blocks that overflow the scale range saturate: u is
+ * clamped to 448 and |x * r| to 6).
+ *
+ *   A, m, w_packed, w_global, n, k as for gemm_w4a4; n % 64 == 0 (gate
+ *            columns [0, n/2), up columns [n/2, n)).  Every m runs the
+ *            tiled kernel (no weight-streaming path).
+ *   h_global device float, the encode-form global scale of h (read only).
+ *   h_codes  [m, n/4] bytes, row-major contiguous, 16-byte aligned.
+ *   h_scales [m, n/32] bytes, row-major contiguous.
+ *   h_out    optional (may be null): receives the bf16 h [m, n/2] that was
+ *            quantised, row-major contiguous, 16-byte aligned.
+ */
+int gemm_w4a4_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                                int64_t m, const void* w_packed, const float* w_global, int64_t n, int64_t k,
+                                const float* h_global, uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_out,
+                                nvfp4_stream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* nvfp4_status_string(int status);
 

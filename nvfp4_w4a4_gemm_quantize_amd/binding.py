@@ -34,6 +34,8 @@ _SIGNATURES = {
     "gemm_w4a4": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _int, _i64, _int, _c_p]),
     "gemm_w4a4_fused_segments": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i64, _i64, _int, _c_p, _c_p, _c_p,
                                         _c_p, _c_p, _c_p, _int, _i64, _c_p]),
+    "gemm_w4a4_silu_mul_quantize": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p,
+                                           _c_p, _c_p]),
     "nvfp4_status_string": (ctypes.c_char_p, [_int]),
     "nvfp4_last_hip_error": (_int, []),
 }
@@ -228,3 +230,40 @@ def gemm_w4a4_fused_segments(a_codes, a_scales, a_global, w_packed, n, k, seg_of
                                       _ptr(out), od, _ld(out), _stream())
     _check(rc, "gemm_w4a4_fused_segments")
     return out
+
+
+def gemm_w4a4_silu_mul_quantize(a_codes, a_scales, a_global, w_packed, w_global, n, k, h_global,
+                                h_codes=None, h_scales=None, return_h=False):
+    """Gate/up GEMM with h = silu(gate)*up quantised to NVFP4 in the epilogue with the static scale h_global.
+
+    Returns (h_codes u8 [m, n/4], h_scales u8 [m, n/32]) and, with return_h, also the bf16 h [m, n/2]
+    that was quantised.
+    """
+    lib = load()
+    _dev(a_codes, torch.uint8, "a_codes")
+    _dev(a_scales, torch.uint8, "a_scales")
+    _dev(a_global, torch.float32, "a_global")
+    _dev(w_packed, torch.uint8, "w_packed")
+    _dev(w_global, torch.float32, "w_global")
+    _dev(h_global, torch.float32, "h_global")
+    m = a_codes.shape[0]
+    if a_codes.numel() != m * (k // 2) or a_scales.numel() != m * (k // 16):
+        raise NVFP4Error("a_codes/a_scales do not match [m, k] with k=%d" % k)
+    if w_packed.numel() < nvfp4_packed_weight_bytes(n, k):
+        raise NVFP4Error("w_packed is smaller than the packed size of [%d, %d]" % (n, k))
+    dev = a_codes.device
+    if h_codes is None:
+        h_codes = torch.empty((m, n // 4), dtype=torch.uint8, device=dev)
+    if h_scales is None:
+        h_scales = torch.empty((m, n // 32), dtype=torch.uint8, device=dev)
+    _dev(h_codes, torch.uint8, "h_codes")
+    _dev(h_scales, torch.uint8, "h_scales")
+    if h_codes.numel() != m * (n // 4) or h_scales.numel() != m * (n // 32) or not h_codes.is_contiguous() \
+            or not h_scales.is_contiguous():
+        raise NVFP4Error("h_codes/h_scales must be contiguous [m, n/4] and [m, n/32]")
+    h = torch.empty((m, n // 2), dtype=torch.bfloat16, device=dev) if return_h else None
+    rc = lib.gemm_w4a4_silu_mul_quantize(_ptr(a_codes), _ptr(a_scales), _ptr(a_global), m, _ptr(w_packed),
+                                         _ptr(w_global), n, k, _ptr(h_global), _ptr(h_codes), _ptr(h_scales),
+                                         _ptr(h), _stream())
+    _check(rc, "gemm_w4a4_silu_mul_quantize")
+    return (h_codes, h_scales, h) if return_h else (h_codes, h_scales)

@@ -110,6 +110,31 @@ int gemm_w4a4_fused_segments(const uint8_t* a_codes, const uint8_t* a_scales, co
                                 (hipStream_t)stream));
 }
 
+int gemm_w4a4_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t m,
+                                const void* w_packed, const float* w_global, int64_t n, int64_t k,
+                                const float* h_global, uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_out,
+                                nvfp4_stream_t stream) {
+  int rc = validate_gemm_silu_quantize(a_codes, a_scales, a_global, m, w_packed, w_global, n, k, h_global, h_codes,
+                                       h_scales, h_out);
+  if (rc || m == 0) return rc;
+  EpilogueArgs epi{};
+  epi.segs.num = 1;
+  epi.segs.off[0] = 0;
+  epi.segs.off[1] = n;
+  epi.seg_epi[0] = NVFP4_SEG_NONE;
+  epi.seg_w_global = w_global;
+  epi.a_global = a_global;
+  epi.silu_mul = 1;
+  epi.out_bf16 = 1;
+  epi.ld_out = n / 2;
+  epi.h_global = h_global;
+  epi.h_codes = h_codes;
+  epi.h_scales = h_scales;
+  epi.h_out = h_out;
+  return hip_status(launch_gemm_tiled(a_codes, a_scales, m, static_cast<const uint8_t*>(w_packed), n, k, nullptr,
+                                      epi, (hipStream_t)stream));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

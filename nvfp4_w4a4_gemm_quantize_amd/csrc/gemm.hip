@@ -158,10 +158,60 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
   };
 
   const float alpha_silu = SILU ? 1.0f / (ga * epi.seg_w_global[0]) : 0.0f;
+  // Quantising SiLU*mul: lane (r, h) takes row r, columns 16h..16h+15 of the
+  // staged fragment -- one whole 16-element block of h.
+  const bool quant = SILU && epi.h_codes != nullptr;
+  const float hg = quant ? *epi.h_global : 0.0f;
+  auto read_block = [&](float (&v)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = ep[r * EPI_STRIDE + 16 * h + c];
+  };
   for (int f = 0; f < NJ * MF; ++f) {
     const int jj = f / MF, i = f % MF;
     const int c0 = (wave_n * NJ + jj) * 32 + ec;
     const int64_t col0 = col_base + c0;
+    if constexpr (SILU) {
+      if (quant) {
+        float gq[16], uq[16];
+        wave_lds_order();
+        static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
+          constexpr int F = decltype(c)::value;
+          if (f == F) stage_frag(acc[F % MF][F / MF]);
+        });
+        wave_lds_order();
+        read_block(gq);
+        wave_lds_order();
+        static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
+          constexpr int F = decltype(c)::value;
+          if (f == F) stage_frag(acc[F % MF][F / MF + NF / 2]);
+        });
+        wave_lds_order();
+        read_block(uq);
+        // h rounded to bf16 first, then the quantiser's own block arithmetic:
+        // the codes equal those of the bf16 h quantised on its own.
+        uint32_t hb[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          hb[c] = (uint32_t)f32_to_bf16_rne(silu_mul(gq[2 * c] * alpha_silu, uq[2 * c] * alpha_silu)) |
+                  ((uint32_t)f32_to_bf16_rne(silu_mul(gq[2 * c + 1] * alpha_silu, uq[2 * c + 1] * alpha_silu)) << 16);
+        const uint4 lo = make_uint4(hb[0], hb[1], hb[2], hb[3]), hi = make_uint4(hb[4], hb[5], hb[6], hb[7]);
+        uint2 codes;
+        const uint32_t S = quantize_block16(lo, hi, hg, &codes);
+        const int64_t row = m0 + wave_m * MF * 32 + i * 32 + r;
+        const int64_t hcol = col_base + (wave_n * NJ + jj) * 32 + 16 * h;
+        // n/2 is a multiple of 32: a fragment's columns are all inside h or all past it
+        if (row < m && hcol < n / 2) {
+          *reinterpret_cast<uint2*>(epi.h_codes + row * (n / 4) + hcol / 2) = codes;
+          epi.h_scales[row * (n / 32) + hcol / 16] = (uint8_t)S;
+          if (epi.h_out) {
+            uint4* dst = reinterpret_cast<uint4*>(epi.h_out + row * (n / 2) + hcol);
+            dst[0] = lo;
+            dst[1] = hi;
+          }
+        }
+        continue;
+      }
+    }
     float v[4][4];
     wave_lds_order();
     static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
@@ -1489,6 +1539,12 @@ static bool try_decode_fp4(const uint8_t* ac, const uint8_t* as, int64_t m, cons
   if (m <= 2) return launch_decode_fp4<2, false>(ac, as, m, w, n, k, out, epi, st);
   if (m <= 4) return launch_decode_fp4<4, false>(ac, as, m, w, n, k, out, epi, st);
   return false;
+}
+
+hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
+                             int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+  launch_prefill<NVFP4_PREFILL_TILE>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,

@@ -27,6 +27,13 @@ struct EpilogueArgs {
   int silu_mul;                 // 1: out[:, j] = silu(y[:, j]) * y[:, j + n/2]
   int out_bf16;                 // 1: bf16 output, 0: fp32
   int64_t ld_out;
+  // SiLU*mul with NVFP4 output (h_codes != null): h is rounded to bf16 and
+  // quantised with the static global scale *h_global into h_codes [m, n/4]
+  // and h_scales [m, n/32]; h_out (optional) receives the bf16 h [m, n/2].
+  const float* h_global;
+  uint8_t* h_codes;
+  uint8_t* h_scales;
+  uint16_t* h_out;
 };
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -39,5 +46,8 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* c
                          hipStream_t st);
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);
+// The tiled (prefill) kernels for any m; used for the quantising SiLU*mul epilogue.
+hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
+                             int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);
 
 }  // namespace nvfp4

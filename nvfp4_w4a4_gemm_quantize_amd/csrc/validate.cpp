@@ -67,4 +67,19 @@ int validate_gemm_common(const void* a_codes, const void* a_scales, const void* 
   return NVFP4_OK;
 }
 
+int validate_gemm_silu_quantize(const void* a_codes, const void* a_scales, const void* a_global, int64_t m,
+                                const void* w_packed, const void* w_global, int64_t n, int64_t k,
+                                const void* h_global, const void* h_codes, const void* h_scales,
+                                const void* h_out) {
+  if (m < 0 || n <= 0 || k <= 0 || n % 64 != 0) return NVFP4_ESHAPE;
+  if (k % 32 != 0) return k % 16 == 0 ? NVFP4_EUNSUPPORTED : NVFP4_ESHAPE;
+  if (m == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_global || !w_packed || !w_global || !h_global || !h_codes || !h_scales)
+    return NVFP4_EINVAL;
+  if (!aligned16(a_codes) || !aligned16(w_packed) || (reinterpret_cast<uintptr_t>(a_scales) & 3u) ||
+      !aligned16(h_codes) || (h_out && !aligned16(h_out)))
+    return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
 }  // namespace nvfp4

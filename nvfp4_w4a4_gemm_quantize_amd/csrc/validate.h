@@ -16,5 +16,9 @@ int validate_unpack(const void* packed, int64_t n, int64_t k, const void* codes,
 int validate_gemm_common(const void* a_codes, const void* a_scales, const void* a_global, int64_t m,
                          const void* w_packed, int64_t n, int64_t k, const void* out, int out_dtype,
                          int64_t ld_out, int64_t out_cols);
+int validate_gemm_silu_quantize(const void* a_codes, const void* a_scales, const void* a_global, int64_t m,
+                                const void* w_packed, const void* w_global, int64_t n, int64_t k,
+                                const void* h_global, const void* h_codes, const void* h_scales,
+                                const void* h_out);
 
 }  // namespace nvfp4

@@ -37,8 +37,8 @@ def lib():
 def test_header_declares_the_four_entry_points_and_helpers():
     fns = declared_functions()
     for name in ("nvfp4_quantize", "nvfp4_pack_weights", "gemm_w4a4", "gemm_w4a4_fused_segments",
-                 "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights_linear", "nvfp4_status_string",
-                 "nvfp4_last_hip_error"):
+                 "gemm_w4a4_silu_mul_quantize", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights_linear",
+                 "nvfp4_status_string", "nvfp4_last_hip_error"):
         assert name in fns
     assert set(fns) == set(binding.EXPORTED)
 
@@ -143,6 +143,26 @@ def test_fused_segments_validation(lib):
     assert fs(lib, nseg=0, offs=(0,), epis=(0,)) == EINVAL
     assert fs(lib, k=80) == EUNSUPPORTED
     assert fs(lib, m=0, sg=None) == OK
+
+
+def sq(lib, m=64, n=128, k=128, ac=A16, wg=A16, hg=A16, hc=A16, hs=A16, ho=None):
+    return lib.gemm_w4a4_silu_mul_quantize(ac, A16, A16, m, A16, wg, n, k, hg, hc, hs, ho, None)
+
+
+def test_silu_mul_quantize_validation(lib):
+    assert sq(lib, n=96) == ESHAPE              # gate/up halves of whole 32-column fragments: n % 64
+    assert sq(lib, n=0) == ESHAPE
+    assert sq(lib, m=-1) == ESHAPE
+    assert sq(lib, k=48) == EUNSUPPORTED
+    assert sq(lib, k=40) == ESHAPE
+    assert sq(lib, hg=None) == EINVAL           # the static scale of h is required
+    assert sq(lib, hc=None) == EINVAL
+    assert sq(lib, hs=None) == EINVAL
+    assert sq(lib, wg=None) == EINVAL
+    assert sq(lib, ac=MIS) == EALIGN
+    assert sq(lib, hc=0x10008) == EALIGN         # codes rows move as 16-byte-aligned data
+    assert sq(lib, ho=MIS) == EALIGN
+    assert sq(lib, m=0, ac=None, hc=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():
