@@ -13,6 +13,10 @@ already resident in HBM:
     quantize A -> GEMM (N = 17408, K = 5120) on one of 8 rotating copies of
     the packed weight (8 x 50.1 MB > the 256 MB Infinity Cache)
 
+Reported beside the timed step: the decode GEMM at M = 1, 8, 32, 64 (HIP
+graph replays), and the MLP with h quantised in the gate/up epilogue
+(static global scale of h) against its unfused chain.
+
 value = algorithmic GEMM FLOP (2MNK) of the prefill part / its wall time
 (quantizers and epilogues included), in TFLOP/s.  The decode part is
 reported as weight GB/s (packed weight bytes / GEMM time).  Kernel durations
@@ -275,6 +279,56 @@ def progress(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def mlp_fused(torch, B, S, reps=5):
+    """The MLP block with h quantised in the gate/up epilogue (static global scale of h, calibrated as
+    2688/amax(h) on another seeded batch through the unfused path) against the unfused chain of the
+    timed step (gate_up -> bf16 h -> dynamic quantize -> down).  Both start from the quantised A."""
+    from nvfp4_w4a4_gemm_quantize_amd import inputs
+    cal = dev_bf16(torch, inputs.mlp(seed=1, weights=False)["A"])
+    B.nvfp4_quantize(cal, S["qa_g"], True, S["qa_codes"], S["qa_scales"])
+    B.gemm_w4a4(S["qa_codes"], S["qa_scales"], S["qa_g"], S["gu_packed"], S["gu_g"], 34816, 5120,
+                epilogue="silu_mul", out=S["h"])
+    hg = torch.empty(1, dtype=torch.float32, device="cuda")
+    B.nvfp4_quantize(S["h"], hg, True, S["qh_codes"], S["qh_scales"])
+    del cal
+    B.nvfp4_quantize(S["mlp_A"], S["qa_g"], True, S["qa_codes"], S["qa_scales"])
+    y_f = torch.empty_like(S["mlp_out"])
+
+    def unfused():
+        B.gemm_w4a4(S["qa_codes"], S["qa_scales"], S["qa_g"], S["gu_packed"], S["gu_g"], 34816, 5120,
+                    epilogue="silu_mul", out=S["h"])
+        B.nvfp4_quantize(S["h"], S["qh_g"], True, S["qh_codes"], S["qh_scales"])
+        B.gemm_w4a4(S["qh_codes"], S["qh_scales"], S["qh_g"], S["dn_packed"], S["dn_g"], 5120, 17408,
+                    out=S["mlp_out"])
+
+    def gate_up_fused():
+        B.gemm_w4a4_silu_mul_quantize(S["qa_codes"], S["qa_scales"], S["qa_g"], S["gu_packed"], S["gu_g"], 34816,
+                                      5120, hg, h_codes=S["qh_codes"], h_scales=S["qh_scales"])
+
+    def fused():
+        gate_up_fused()
+        B.gemm_w4a4(S["qh_codes"], S["qh_scales"], hg, S["dn_packed"], S["dn_g"], 5120, 17408, out=y_f)
+
+    def time_us(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    t_u, t_f, t_g = time_us(unfused), time_us(fused), time_us(gate_up_fused)
+    dev = float(torch.linalg.vector_norm((y_f.float() - S["mlp_out"].float())) /
+                torch.linalg.vector_norm(S["mlp_out"].float()))
+    return {"static_h_global": round(float(hg.item()), 6), "unfused_us": round(t_u, 1), "fused_us": round(t_f, 1),
+            "gate_up_quantize_fused_us": round(t_g, 1), "saving_frac": round(1.0 - t_f / t_u, 4),
+            "tflops_fused": round((FLOP["gate_up"] + FLOP["down"]) / t_f / 1e6, 1),
+            "down_out_rel_l2_vs_unfused": round(dev, 5)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -307,6 +361,8 @@ def main():
     gemm_ms = dur["gdn"] + dur["gate_up"] + dur["down"]
     achieved = prefill_flop / (gemm_ms * 1e-3) / 1e12
     sweep = None if args.no_decode_sweep else decode_sweep(torch, B, S)
+    fused_mlp = mlp_fused(torch, B, S)
+    progress("fused MLP timed")
     traffic = measured_traffic()
     progress("decode sweep done")
     if args.copy_probe_mib > 0:
@@ -351,6 +407,7 @@ def main():
                    "hbm_frac": round(DECODE_BYTES / (dur["decode"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                    "quantize_plus_gemm_us": round(dur["decode_all"] * 1e3, 2),
                    "sweep": sweep},
+        "mlp_fused_h_quantize": fused_mlp,
         "setup_s": round(S["setup_s"], 1),
     }
     if not args.no_cpu_baseline:
