@@ -37,6 +37,9 @@ Modules
               second implementation used to pin ``quantize``).
 ``gemm``      fp64 dequantisation, W4A4 GEMM, the sum(|a*b|) error bound.
 ``epilogue``  fp64 SiLU*mul, sigmoid and Gated-DeltaNet decay epilogues.
+``mechanism`` the coarser-scaled reference formats (E4M3 scale per B
+              elements; one per-tensor scale) and the error measures of the
+              pages' mechanism study.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against brute force, closed forms, library routines or hand-worked examples;
