@@ -37,6 +37,8 @@ Modules
               second implementation used to pin ``quantize``).
 ``gemm``      fp64 dequantisation, W4A4 GEMM, the sum(|a*b|) error bound.
 ``epilogue``  fp64 SiLU*mul, sigmoid and Gated-DeltaNet decay epilogues.
+``recurrence`` the gated delta-rule recurrence of a Gated DeltaNet layer
+              (fp64), the second workload.
 ``mechanism`` the coarser-scaled reference formats (E4M3 scale per B
               elements; one per-tensor scale) and the error measures of the
               pages' mechanism study.
