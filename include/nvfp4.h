@@ -220,6 +220,38 @@ int gemm_w4a4_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
                                 const float* h_global, uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_out,
                                 nvfp4_stream_t stream);
 
+/*
+ * gdn_recurrence -- the gated delta-rule recurrence of a Gated DeltaNet layer,
+ * the recurrent half that the in-projection feeds.  The pages describe it by
+ * its mechanism: every write overwrites the state along the current key
+ * direction, so injected noise plateaus and a state impulse is forgotten
+ * (bayesiansapien page, "The four-part mechanism study", third item).  The
+ * rule computed (the standard gated delta rule), per value head h with key
+ * head h / (hv / hk) and fp32 state S [head_dim, head_dim] (row = value
+ * index, column = key index), for t = 0 .. T-1:
+ *     k^ = k_t / sqrt(|k_t|^2 + 1e-6),  q^ = q_t / sqrt(|q_t|^2 + 1e-6),
+ *     S <- exp(g_t) S (I - beta_t k^ k^T) + beta_t v_t k^T,   o_t = S q^.
+ * beta and g are the outputs of the fused in-projection's SIGMOID and
+ * GDN_DECAY segments; q, k, v its first three segments, so every input may
+ * point into that one bf16 buffer with its row stride.
+ *
+ *   q, k      bf16 [T, hk * head_dim], row strides ld_q, ld_k (elements,
+ *             multiples of 8); 16-byte aligned.
+ *   v         bf16 [T, hv * head_dim], row stride ld_v (multiple of 8).
+ *   beta, g   bf16 [T, hv], row strides ld_beta, ld_g.
+ *   T >= 0 (0 enqueues nothing); hk >= 1; hv a multiple of hk;
+ *   head_dim  128 (others: NVFP4_EUNSUPPORTED).
+ *   s_init    optional fp32 [hv, head_dim, head_dim] initial state (null = 0).
+ *   s_final   optional fp32 [hv, head_dim, head_dim], receives the last state.
+ *   out       [T, hv * head_dim] fp32 or bf16 (out_dtype), row stride ld_out.
+ * The state stays in fp32 registers for the whole sequence; results are
+ * deterministic.
+ */
+int gdn_recurrence(const uint16_t* q, int64_t ld_q, const uint16_t* k, int64_t ld_k, const uint16_t* v,
+                   int64_t ld_v, const uint16_t* beta, int64_t ld_beta, const uint16_t* g, int64_t ld_g,
+                   int64_t T, int hk, int hv, int head_dim, const float* s_init, float* s_final, void* out,
+                   int out_dtype, int64_t ld_out, nvfp4_stream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* nvfp4_status_string(int status);
 

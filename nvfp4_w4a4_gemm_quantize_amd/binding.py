@@ -36,6 +36,8 @@ _SIGNATURES = {
                                         _c_p, _c_p, _c_p, _int, _i64, _c_p]),
     "gemm_w4a4_silu_mul_quantize": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p,
                                            _c_p, _c_p]),
+    "gdn_recurrence": (_int, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _i64, _i64, _int, _int, _int,
+                              _c_p, _c_p, _c_p, _int, _i64, _c_p]),
     "nvfp4_status_string": (ctypes.c_char_p, [_int]),
     "nvfp4_last_hip_error": (_int, []),
 }
@@ -267,3 +269,35 @@ def gemm_w4a4_silu_mul_quantize(a_codes, a_scales, a_global, w_packed, w_global,
                                          _ptr(h), _stream())
     _check(rc, "gemm_w4a4_silu_mul_quantize")
     return (h_codes, h_scales, h) if return_h else (h_codes, h_scales)
+
+
+def _ld2(t, name):
+    """Row stride (elements) of a 2-D bf16 view with unit column stride."""
+    _dev(t, torch.bfloat16, name)
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise NVFP4Error("%s must be a 2-D view with unit column stride" % name)
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def gdn_recurrence(q, k, v, beta, g, hk, hv, s_init=None, return_state=False, out_dtype=torch.float32, out=None):
+    """Gated delta rule over T steps.  q, k [T, hk*128], v [T, hv*128], beta, g [T, hv]: bf16 2-D views
+    (they may be column slices of the fused in-projection output).  Returns o [T, hv*128] (and the final
+    fp32 state [hv, 128, 128] with return_state)."""
+    lib = load()
+    T = q.shape[0]
+    lds = [_ld2(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (g, "g"))]
+    if any(x.shape[0] != T for x in (k, v, beta, g)):
+        raise NVFP4Error("q, k, v, beta, g must have the same number of rows")
+    if q.shape[1] != hk * 128 or k.shape[1] != hk * 128 or v.shape[1] != hv * 128 or beta.shape[1] != hv \
+            or g.shape[1] != hv:
+        raise NVFP4Error("shapes must be q, k [T, hk*128], v [T, hv*128], beta, g [T, hv]")
+    if s_init is not None:
+        _dev(s_init, torch.float32, "s_init")
+        if s_init.shape != (hv, 128, 128) or not s_init.is_contiguous():
+            raise NVFP4Error("s_init must be contiguous fp32 [hv, 128, 128]")
+    s_final = torch.empty((hv, 128, 128), dtype=torch.float32, device=q.device) if return_state else None
+    out, od = _out(out, T, hv * 128, out_dtype, q.device)
+    rc = lib.gdn_recurrence(_ptr(q), lds[0], _ptr(k), lds[1], _ptr(v), lds[2], _ptr(beta), lds[3], _ptr(g), lds[4],
+                            T, hk, hv, 128, _ptr(s_init), _ptr(s_final), _ptr(out), od, _ld(out), _stream())
+    _check(rc, "gdn_recurrence")
+    return (out, s_final) if return_state else out

@@ -135,6 +135,35 @@ int gemm_w4a4_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
                                       epi, (hipStream_t)stream));
 }
 
+int gdn_recurrence(const uint16_t* q, int64_t ld_q, const uint16_t* k, int64_t ld_k, const uint16_t* v, int64_t ld_v,
+                   const uint16_t* beta, int64_t ld_beta, const uint16_t* g, int64_t ld_g, int64_t T, int hk, int hv,
+                   int head_dim, const float* s_init, float* s_final, void* out, int out_dtype, int64_t ld_out,
+                   nvfp4_stream_t stream) {
+  int rc = validate_gdn_recurrence(q, ld_q, k, ld_k, v, ld_v, beta, ld_beta, g, ld_g, T, hk, hv, head_dim, s_init,
+                                   s_final, out, out_dtype, ld_out);
+  if (rc || T == 0) return rc;
+  GdnArgs a{};
+  a.q = q;
+  a.ld_q = ld_q;
+  a.k = k;
+  a.ld_k = ld_k;
+  a.v = v;
+  a.ld_v = ld_v;
+  a.beta = beta;
+  a.ld_beta = ld_beta;
+  a.g = g;
+  a.ld_g = ld_g;
+  a.T = T;
+  a.hk = hk;
+  a.hv = hv;
+  a.s_init = s_init;
+  a.s_final = s_final;
+  a.o = out;
+  a.o_bf16 = out_dtype == NVFP4_OUT_BF16;
+  a.ld_o = ld_out;
+  return hip_status(launch_gdn_recurrence(a, (hipStream_t)stream));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

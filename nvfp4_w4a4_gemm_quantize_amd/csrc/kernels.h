@@ -46,6 +46,30 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* c
                          hipStream_t st);
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);
+// Gated delta-rule recurrence (head dimension 128): bf16 inputs with row
+// strides in elements, fp32 state [hv, 128, 128], output [T, hv * 128].
+struct GdnArgs {
+  const uint16_t* q;
+  int64_t ld_q;
+  const uint16_t* k;
+  int64_t ld_k;
+  const uint16_t* v;
+  int64_t ld_v;
+  const uint16_t* beta;
+  int64_t ld_beta;
+  const uint16_t* g;
+  int64_t ld_g;
+  int64_t T;
+  int hk;
+  int hv;
+  const float* s_init;
+  float* s_final;
+  void* o;
+  int o_bf16;
+  int64_t ld_o;
+};
+hipError_t launch_gdn_recurrence(const GdnArgs& a, hipStream_t st);
+
 // The tiled (prefill) kernels for any m; used for the quantising SiLU*mul epilogue.
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                              int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);

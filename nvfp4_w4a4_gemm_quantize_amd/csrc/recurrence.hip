@@ -1,0 +1,228 @@
+// Gated delta-rule recurrence of a Gated DeltaNet layer on gfx950: the
+// second workload of the path, fed by the fused in-projection (its q, k, v
+// columns and the sigmoid / decay gate columns).  The pages describe the
+// rule by its behaviour -- each write overwrites the state along the current
+// key direction (bayesiansapien page, "The four-part mechanism study", third
+// item); per value head h, with key head h / (Hv / Hk) and state S [128, 128]
+// (row = value index, column = key index):
+//     k^ = k / sqrt(|k|^2 + 1e-6),  q^ likewise,  alpha = exp(g),
+//     u = alpha S k^,  c = beta (v - u),  S <- alpha S + c k^T,  o = S q^.
+// Since the dot products are taken on the state before the step,
+//     u_i = alpha (S_i . k^),  o_i = alpha (S_i . q^) + c_i (k^ . q^),
+// both dots of a row come from one pass over the old state, and the update is
+// one multiply-add per element.
+//
+// Work split: the recurrence is sequential in time and independent per state
+// row, so a workgroup owns 16 rows of one head's state in registers for the
+// whole sequence (8 workgroups per head).  16 lanes share a row, each holding
+// 8 of its 128 columns (4j..4j+3 and 64+4j..64+4j+3 for lane j, so the 16
+// lanes' 16-byte LDS reads of a key are contiguous); the row's dot products
+// are summed across those lanes with DPP.  Inputs are staged 32 time steps at
+// a time through double-buffered LDS: while a chunk is being consumed the
+// next one is loaded into registers, then converted -- keys and queries to
+// normalised fp32 (their norms reduced once per step per workgroup), gates to
+// (alpha, beta, k^.q^) -- and written to the other buffer.  ALU-bound: about
+// 7 * 128^2 flops per head per token.
+#include "kernels.h"
+#include "nvfp4_device.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kD = 128;          // key and value dimension of a head
+constexpr int kRows = 16;        // state rows per workgroup
+constexpr int kThreads = 256;    // 4 waves x 4 rows x 16 lanes
+constexpr int kChunk = 32;       // time steps per LDS stage
+constexpr float kNormEps = 1e-6f;
+
+struct Stage {
+  float kn[kChunk][kD];     // normalised keys
+  float qn[kChunk][kD];     // normalised queries
+  float v[kChunk][kRows];   // this workgroup's value rows
+  float4 sc[kChunk];        // alpha, beta, k^ . q^, unused
+};
+
+__device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a DPP row; every lane gets the same bits (each
+// step adds the same two values in either order).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);   // row_half_mirror
+  x += dpp<0x140>(x);   // row_mirror
+  return x;
+}
+
+// Registers holding one chunk's raw inputs between its global loads and its
+// conversion into a Stage.  Thread t carries key and query pieces (8 bf16) of
+// steps t/16 and 16 + t/16, piece t%16; threads < 64 a value half-row (8
+// bf16) of step t/2; threads < kChunk the two gates of step t.
+struct Raw {
+  uint4 k[2], q[2], v;
+  uint32_t beta, g;
+};
+
+}  // namespace
+
+__global__ void __launch_bounds__(kThreads)
+gdn_recurrence_kernel(GdnArgs a) {
+  __shared__ Stage st[2];
+  __shared__ float obuf[kChunk][kRows];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int lr = lane & 15;                     // lane within the row
+  const int rloc = wave * 4 + (lane >> 4);      // row within the workgroup
+  const int groups = kD / kRows;
+  const int h = blockIdx.x / groups;
+  const int i0 = (blockIdx.x % groups) * kRows;
+  const int hk = h / (a.hv / a.hk);
+  const int64_t T = a.T;
+  const int64_t nchunks = (T + kChunk - 1) / kChunk;
+
+  const int c0 = 4 * lr, c1 = 64 + 4 * lr;      // this lane's columns
+  float s[8];
+  if (a.s_init) {
+    const float* p = a.s_init + ((int64_t)h * kD + i0 + rloc) * kD;
+    const float4 x = *reinterpret_cast<const float4*>(p + c0), y = *reinterpret_cast<const float4*>(p + c1);
+    s[0] = x.x; s[1] = x.y; s[2] = x.z; s[3] = x.w; s[4] = y.x; s[5] = y.y; s[6] = y.z; s[7] = y.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = 0.0f;
+  }
+
+  auto load = [&](int64_t chunk, Raw& R) __attribute__((always_inline)) {
+    const int64_t t0 = chunk * kChunk;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      int64_t step = t0 + p * 16 + (t >> 4);
+      step = step < T ? step : T - 1;
+      const int col = hk * kD + 8 * (t & 15);
+      R.k[p] = *reinterpret_cast<const uint4*>(a.k + step * a.ld_k + col);
+      R.q[p] = *reinterpret_cast<const uint4*>(a.q + step * a.ld_q + col);
+    }
+    if (t < 2 * kChunk) {
+      int64_t step = t0 + (t >> 1);
+      step = step < T ? step : T - 1;
+      R.v = *reinterpret_cast<const uint4*>(a.v + step * a.ld_v + (int64_t)h * kD + i0 + 8 * (t & 1));
+    }
+    if (t < kChunk) {
+      int64_t step = t0 + t;
+      step = step < T ? step : T - 1;
+      R.beta = a.beta[step * a.ld_beta + h];
+      R.g = a.g[step * a.ld_g + h];
+    }
+  };
+  auto unpack8 = [](const uint4& u, float (&f)[8]) __attribute__((always_inline)) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16f(w[e] & 0xFFFFu);
+      f[2 * e + 1] = bf16f(w[e] >> 16);
+    }
+  };
+  auto store = [&](const Raw& R, Stage& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int step = p * 16 + (t >> 4), pc = t & 15;
+      float kf[8], qf[8];
+      unpack8(R.k[p], kf);
+      unpack8(R.q[p], qf);
+      float kk = 0.0f, qq = 0.0f, kq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kk = fmaf(kf[e], kf[e], kk);
+        qq = fmaf(qf[e], qf[e], qq);
+        kq = fmaf(kf[e], qf[e], kq);
+      }
+      kk = row_sum16(kk);
+      qq = row_sum16(qq);
+      kq = row_sum16(kq);
+      const float nk = 1.0f / sqrtf(kk + kNormEps), nq = 1.0f / sqrtf(qq + kNormEps);
+      float4* kd = reinterpret_cast<float4*>(&S.kn[step][8 * pc]);
+      float4* qd = reinterpret_cast<float4*>(&S.qn[step][8 * pc]);
+      kd[0] = make_float4(kf[0] * nk, kf[1] * nk, kf[2] * nk, kf[3] * nk);
+      kd[1] = make_float4(kf[4] * nk, kf[5] * nk, kf[6] * nk, kf[7] * nk);
+      qd[0] = make_float4(qf[0] * nq, qf[1] * nq, qf[2] * nq, qf[3] * nq);
+      qd[1] = make_float4(qf[4] * nq, qf[5] * nq, qf[6] * nq, qf[7] * nq);
+      if (pc == 0) S.sc[step].z = kq * nk * nq;
+    }
+    if (t < 2 * kChunk) {
+      float vf[8];
+      unpack8(R.v, vf);
+      float4* vd = reinterpret_cast<float4*>(&S.v[t >> 1][8 * (t & 1)]);
+      vd[0] = make_float4(vf[0], vf[1], vf[2], vf[3]);
+      vd[1] = make_float4(vf[4], vf[5], vf[6], vf[7]);
+    }
+    if (t < kChunk) {
+      S.sc[t].x = expf(bf16f(R.g & 0xFFFFu));
+      S.sc[t].y = bf16f(R.beta & 0xFFFFu);
+    }
+  };
+
+  Raw R;
+  load(0, R);
+  store(R, st[0]);
+  __syncthreads();
+  for (int64_t c = 0; c < nchunks; ++c) {
+    if (c + 1 < nchunks) load(c + 1, R);
+    const Stage& S = st[c & 1];
+    const int cnt = (int)(T - c * kChunk < kChunk ? T - c * kChunk : kChunk);
+#pragma unroll 2
+    for (int step = 0; step < cnt; ++step) {
+      const float4 ka = reinterpret_cast<const float4*>(S.kn[step])[lr];
+      const float4 kb = reinterpret_cast<const float4*>(S.kn[step])[16 + lr];
+      const float4 qa = reinterpret_cast<const float4*>(S.qn[step])[lr];
+      const float4 qb = reinterpret_cast<const float4*>(S.qn[step])[16 + lr];
+      const float4 sc = S.sc[step];
+      const float vi = S.v[step][rloc];
+      float sk0 = s[0] * ka.x, sk1 = s[1] * ka.y, sq0 = s[0] * qa.x, sq1 = s[1] * qa.y;
+      sk0 = fmaf(s[2], ka.z, sk0); sk1 = fmaf(s[3], ka.w, sk1);
+      sq0 = fmaf(s[2], qa.z, sq0); sq1 = fmaf(s[3], qa.w, sq1);
+      sk0 = fmaf(s[4], kb.x, sk0); sk1 = fmaf(s[5], kb.y, sk1);
+      sq0 = fmaf(s[4], qb.x, sq0); sq1 = fmaf(s[5], qb.y, sq1);
+      sk0 = fmaf(s[6], kb.z, sk0); sk1 = fmaf(s[7], kb.w, sk1);
+      sq0 = fmaf(s[6], qb.z, sq0); sq1 = fmaf(s[7], qb.w, sq1);
+      const float sk = row_sum16(sk0 + sk1), sq = row_sum16(sq0 + sq1);
+      const float alpha = sc.x, beta = sc.y;
+      const float cw = beta * (vi - alpha * sk);
+      const float o = fmaf(alpha, sq, cw * sc.z);
+      const float kv[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[j] = fmaf(alpha, s[j], cw * kv[j]);
+      if (lr == 0) obuf[step][rloc] = o;
+    }
+    __syncthreads();
+    if (c + 1 < nchunks) store(R, st[(c + 1) & 1]);
+    // this chunk's outputs: kChunk x 16 values, two per thread
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = t + e * kThreads, step = idx >> 4, r = idx & 15;
+      if (step < cnt) {
+        const int64_t off = (c * kChunk + step) * a.ld_o + (int64_t)h * kD + i0 + r;
+        const float val = obuf[step][r];
+        if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[off] = f32_to_bf16_rne(val);
+        else reinterpret_cast<float*>(a.o)[off] = val;
+      }
+    }
+    __syncthreads();
+  }
+  if (a.s_final) {
+    float* p = a.s_final + ((int64_t)h * kD + i0 + rloc) * kD;
+    *reinterpret_cast<float4*>(p + c0) = make_float4(s[0], s[1], s[2], s[3]);
+    *reinterpret_cast<float4*>(p + c1) = make_float4(s[4], s[5], s[6], s[7]);
+  }
+}
+
+hipError_t launch_gdn_recurrence(const GdnArgs& a, hipStream_t st) {
+  const unsigned blocks = (unsigned)(a.hv * (kD / kRows));
+  hipLaunchKernelGGL(gdn_recurrence_kernel, dim3(blocks), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -82,4 +82,24 @@ int validate_gemm_silu_quantize(const void* a_codes, const void* a_scales, const
   return NVFP4_OK;
 }
 
+int validate_gdn_recurrence(const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v, int64_t ld_v,
+                            const void* beta, int64_t ld_beta, const void* g, int64_t ld_g, int64_t T, int hk,
+                            int hv, int head_dim, const void* s_init, const void* s_final, const void* out,
+                            int out_dtype, int64_t ld_out) {
+  if (T < 0 || hk <= 0 || hv <= 0 || hv % hk != 0) return NVFP4_ESHAPE;
+  if (head_dim != 128) return head_dim > 0 ? NVFP4_EUNSUPPORTED : NVFP4_ESHAPE;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_EINVAL;
+  if (ld_q < (int64_t)hk * 128 || ld_k < (int64_t)hk * 128 || ld_v < (int64_t)hv * 128 || ld_beta < hv ||
+      ld_g < hv || ld_out < (int64_t)hv * 128)
+    return NVFP4_ESHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!q || !k || !v || !beta || !g || !out) return NVFP4_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (ld_q % 8) || (ld_k % 8) || (ld_v % 8) ||
+      (reinterpret_cast<uintptr_t>(beta) & 1u) || (reinterpret_cast<uintptr_t>(g) & 1u) ||
+      (s_init && !aligned16(s_init)) || (s_final && !aligned16(s_final)) ||
+      (reinterpret_cast<uintptr_t>(out) & (out_dtype == NVFP4_OUT_F32 ? 3u : 1u)))
+    return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
 }  // namespace nvfp4

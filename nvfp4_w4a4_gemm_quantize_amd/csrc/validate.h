@@ -20,5 +20,9 @@ int validate_gemm_silu_quantize(const void* a_codes, const void* a_scales, const
                                 const void* w_packed, const void* w_global, int64_t n, int64_t k,
                                 const void* h_global, const void* h_codes, const void* h_scales,
                                 const void* h_out);
+int validate_gdn_recurrence(const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v, int64_t ld_v,
+                            const void* beta, int64_t ld_beta, const void* g, int64_t ld_g, int64_t T, int hk,
+                            int hv, int head_dim, const void* s_init, const void* s_final, const void* out,
+                            int out_dtype, int64_t ld_out);
 
 }  // namespace nvfp4

@@ -19,6 +19,11 @@ gdn_inproj  M=4096 K=5120; q 2048 | k 2048 | v 6144 | z 6144 | b 48 | a 48;
             (max/min scale ratio exactly 8); A_log, dt_bias ~ N(0, 0.5) [48]
 decode      M in {1, 8, 32, 64}, N=17408, K=5120; A ~ N(0,1) with 5 outlier
             channels x50; W ~ N(0, 1/sqrt(K))
+recurrence  gated delta rule over T tokens, 16 key heads / 48 value heads of
+            dimension 128 (the in-projection's q | k | v split): q, k, v ~
+            N(0, 1); write strength beta ~ U(0, 1); log-decay g = -r with r
+            log-uniform on [1e-4, 1e-1] (decay factors 0.905 .. 0.9999, the
+            long-memory regime where an accumulating state would grow)
 
 N(mu, sigma) takes sigma as the standard deviation.  Every stream is seeded
 by (seed, name) so any tensor can be regenerated on its own.
@@ -139,4 +144,14 @@ def decode(M, seed=0, weights=True):
     out = dict(A=normal_activations(M, s["K"], "decode/A%d" % M, seed))
     if weights:
         out["W"] = normal((s["N"], s["K"]), 1.0 / np.sqrt(s["K"]), "decode/W", seed)
+    return out
+
+
+def recurrence(T, hk=16, hv=48, seed=0, d=128):
+    """Inputs of the gated delta rule: bf16 bits q, k [T, hk*d], v [T, hv*d], beta, g [T, hv]."""
+    out = dict(q=normal((T, hk * d), 1.0, "rec/q", seed), k=normal((T, hk * d), 1.0, "rec/k", seed),
+               v=normal((T, hv * d), 1.0, "rec/v", seed))
+    out["beta"] = f32_to_bf16_bits(rng("rec/beta", seed).uniform(0.0, 1.0, (T, hv)).astype(np.float32))
+    r = np.exp(rng("rec/g", seed).uniform(np.log(1e-4), np.log(1e-1), (T, hv)))
+    out["g"] = f32_to_bf16_bits((-r).astype(np.float32))
     return out

@@ -44,11 +44,12 @@ def key_head_of(hv, hk):
     return np.arange(hv) // (hv // hk)
 
 
-def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False):
+def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False, return_row_l1=False):
     """Run the gated delta rule.
 
     q, k  [T, Hk, d_k]; v [T, Hv, d_v]; beta, g [T, Hv]; s_init [Hv, d_v, d_k] or None (zeros).
-    Returns (o [T, Hv, d_v], S_final [Hv, d_v, d_k]) and, with return_states, the list of states.
+    Returns (o [T, Hv, d_v], S_final [Hv, d_v, d_k]) and, with return_states, the list of states;
+    with return_row_l1 (instead), the row L1 norms sum_j |S_t[h, i, j]| [T, Hv, d_v] after each step.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -61,6 +62,7 @@ def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False):
     S = np.zeros((hv, dv, dk)) if s_init is None else np.array(s_init, dtype=np.float64)
     o = np.empty((T, hv, dv))
     states = []
+    row_l1 = np.empty((T, hv, dv)) if return_row_l1 else None
     for t in range(T):
         kn = l2_normalize(k[t], eps)[kh]                  # [Hv, d_k]
         qn = l2_normalize(q[t], eps)[kh]
@@ -71,7 +73,35 @@ def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False):
         o[t] = np.einsum("hij,hj->hi", S, qn)
         if return_states:
             states.append(S.copy())
-    return (o, S, states) if return_states else (o, S)
+        if return_row_l1:
+            row_l1[t] = np.sum(np.abs(S), axis=2)
+    if return_states:
+        return o, S, states
+    return (o, S, row_l1) if return_row_l1 else (o, S)
+
+
+def fp32_tolerance(row_l1, v, s_init=None, out_is_bf16=False, o_ref=None):
+    """Per-element bound for an fp32 evaluation of the recurrence, [T, Hv, d_v].
+
+    Each step forms two 128-term dot products of a state row (with a key and a
+    query of norm <= 1) and one multiply-add per element; with unit roundoff
+    u = 2^-24 the error it adds to row i is at most c u (|S_i|_1 + |v_i|), with
+    c = 64 covering the dot-product length's rounding (the key's and query's own
+    normalisation errors included), and earlier errors are not amplified
+    because every step's map S -> alpha S (I - beta k^ k^T) has norm <= 1.  So
+    after t + 1 steps |o_t,i - o~| <= (t + 1) c u max_{tau <= t}(|S_tau,i|_1 + |v_tau,i|),
+    plus the state's initial magnitude, plus the bf16 rounding of the output
+    when it is bf16 (unit roundoff 2^-8: 8 significand bits, round to nearest).
+    """
+    u = 2.0 ** -24
+    T = row_l1.shape[0]
+    m = np.maximum.accumulate(row_l1 + np.abs(np.asarray(v, dtype=np.float64)), axis=0)
+    if s_init is not None:
+        m = np.maximum(m, np.sum(np.abs(np.asarray(s_init, dtype=np.float64)), axis=2)[None])
+    tol = (np.arange(1, T + 1, dtype=np.float64)[:, None, None]) * 64 * u * m
+    if out_is_bf16:
+        tol = tol + 2.0 ** -8 * (np.abs(o_ref) + tol)
+    return tol
 
 
 def step_matrix_form(S, q, k, v, beta, g, eps=EPS):

@@ -37,7 +37,8 @@ def lib():
 def test_header_declares_the_four_entry_points_and_helpers():
     fns = declared_functions()
     for name in ("nvfp4_quantize", "nvfp4_pack_weights", "gemm_w4a4", "gemm_w4a4_fused_segments",
-                 "gemm_w4a4_silu_mul_quantize", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights_linear",
+                 "gemm_w4a4_silu_mul_quantize", "gdn_recurrence", "nvfp4_packed_weight_bytes",
+                 "nvfp4_unpack_weights_linear",
                  "nvfp4_status_string", "nvfp4_last_hip_error"):
         assert name in fns
     assert set(fns) == set(binding.EXPORTED)
@@ -163,6 +164,33 @@ def test_silu_mul_quantize_validation(lib):
     assert sq(lib, hc=0x10008) == EALIGN         # codes rows move as 16-byte-aligned data
     assert sq(lib, ho=MIS) == EALIGN
     assert sq(lib, m=0, ac=None, hc=None) == OK
+
+
+def rec(lib, q=A16, ldq=256, k=A16, ldk=256, v=A16, ldv=768, b=A16, ldb=6, g=A16, ldg=6, T=10, hk=2, hv=6, d=128,
+        si=None, sf=None, out=A16, dt=0, ldo=768):
+    return lib.gdn_recurrence(q, ldq, k, ldk, v, ldv, b, ldb, g, ldg, T, hk, hv, d, si, sf, out, dt, ldo, None)
+
+
+def test_gdn_recurrence_validation(lib):
+    assert rec(lib, hv=5) == ESHAPE            # value heads a multiple of key heads
+    assert rec(lib, hk=0) == ESHAPE
+    assert rec(lib, T=-1) == ESHAPE
+    assert rec(lib, d=64) == EUNSUPPORTED      # head dimension 128 only
+    assert rec(lib, d=0) == ESHAPE
+    assert rec(lib, dt=3) == EINVAL
+    assert rec(lib, ldq=200) == ESHAPE         # rows shorter than hk * 128
+    assert rec(lib, ldv=700) == ESHAPE
+    assert rec(lib, ldb=5) == ESHAPE
+    assert rec(lib, ldo=512) == ESHAPE
+    assert rec(lib, q=None) == EINVAL
+    assert rec(lib, g=None) == EINVAL
+    assert rec(lib, out=None) == EINVAL
+    assert rec(lib, k=MIS) == EALIGN
+    assert rec(lib, ldk=260) == EALIGN         # 16-byte row pieces need ld % 8 == 0
+    assert rec(lib, b=0x10001) == EALIGN
+    assert rec(lib, si=MIS) == EALIGN
+    assert rec(lib, out=0x10002, dt=0) == EALIGN
+    assert rec(lib, T=0, q=None, out=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():
