@@ -29,16 +29,31 @@ struct ColumnEpilogue {
   float dt_bias;
 };
 
+// The column's segment by a scan over the segment table.  The table and the
+// segments' scales and gate types are read at wave-uniform addresses (scalar
+// loads, no dependent chain); each lane only selects.  Columns of the decay
+// segment also read their head's A_log and dt_bias.
 __device__ __forceinline__ ColumnEpilogue column_epilogue(const EpilogueArgs& e, int64_t col, float ga) {
-  int s = 0;
-  while (s + 1 < e.segs.num && col >= e.segs.off[s + 1]) ++s;
+  float gw = e.seg_w_global[0];
+  int type = e.seg_epi[0];
+  int64_t first = 0;
+  for (int s = 1; s < e.segs.num; ++s) {
+    const int64_t o = e.segs.off[s];
+    const float g = e.seg_w_global[s];
+    const int t = e.seg_epi[s];
+    if (col >= o) {
+      gw = g;
+      type = t;
+      first = o;
+    }
+  }
   ColumnEpilogue c;
-  c.alpha = 1.0f / (ga * e.seg_w_global[s]);
-  c.type = e.seg_epi[s];
+  c.alpha = 1.0f / (ga * gw);
+  c.type = type;
   c.exp_alog = 0.0f;
   c.dt_bias = 0.0f;
-  if (c.type == 2) {
-    const int64_t h = col - e.segs.off[s];
+  if (type == 2) {
+    const int64_t h = col - first;
     c.exp_alog = expf(e.a_log[h]);
     c.dt_bias = e.dt_bias[h];
   }
@@ -48,26 +63,44 @@ __device__ __forceinline__ ColumnEpilogue column_epilogue(const EpilogueArgs& e,
 // Per-column epilogue parameters of a workgroup's BN output columns
 // (col_base ...), written to LDS once per workgroup before its main loop so
 // the epilogue reads one LDS entry per column instead of searching the
-// segment table and dividing for every output.  Columns past n repeat the
-// last column (their outputs are never stored).
+// segment table and dividing for every output.  Columns past n (never
+// stored) get no gate, so a padded tile does no gate arithmetic for them.
 template <int BN, int NT>
 __device__ __forceinline__ void fill_column_table(ColumnEpilogue* tab, const EpilogueArgs& e, int64_t col_base,
                                                   int64_t n) {
   const float ga = *e.a_global;
   for (int c = (int)threadIdx.x; c < BN; c += NT) {
     const int64_t col = col_base + c;
-    tab[c] = column_epilogue(e, col < n ? col : n - 1, ga);
+    ColumnEpilogue ce = column_epilogue(e, col < n ? col : n - 1, ga);
+    if (col >= n) ce.type = 0;
+    tab[c] = ce;
   }
+}
+
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+// 1 / (1 + e^-y) on the hardware exp2 and reciprocal.
+__device__ __forceinline__ float sigmoid_f(float y) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * kLog2e));
+}
+
+// log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  log1p(e) is taken as
+// log(u) * e / (u - 1) with u = 1 + e rounded (u - 1 is exact), which keeps
+// the relative accuracy of small e; u == 1 gives e itself.
+__device__ __forceinline__ float softplus_f(float x) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float u = 1.0f + e;
+  const float l = u == 1.0f ? e : __builtin_amdgcn_logf(u) * kLn2 * e * __builtin_amdgcn_rcpf(u - 1.0f);
+  return fmaxf(x, 0.0f) + l;
 }
 
 __device__ __forceinline__ float apply_epilogue(const ColumnEpilogue& c, float acc) {
   float y = acc * c.alpha;
   if (c.type == 1) {
-    y = 1.0f / (1.0f + expf(-y));
+    y = sigmoid_f(y);
   } else if (c.type == 2) {
-    const float x = y + c.dt_bias;
-    const float sp = x > 20.0f ? x : log1pf(expf(x));
-    y = -c.exp_alog * sp;
+    y = -c.exp_alog * softplus_f(y + c.dt_bias);
   }
   return y;
 }
