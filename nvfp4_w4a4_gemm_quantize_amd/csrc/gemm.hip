@@ -572,32 +572,22 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
 #endif
 
 // Which output tile a workgroup of the prefill kernel computes (1-D grids).
-// sub == 0: tile first + blockIdx.x of a row-major grid gx tiles wide.
-// sub == 1: the workgroup's tile is half as tall; two workgroups cover each
-//           tile first + blockIdx.x / 2 of the gx-wide grid of full tiles.
-// sub == 2: the workgroup's tile is half as tall and half as wide; four
-//           workgroups cover each tile first + blockIdx.x / 4.
-// (sub > 0 serves the last, partly filled round of a launch.)
+// A full tile is `first + blockIdx.x / (ry * rx)` of a row-major grid gx full
+// tiles wide; the workgroup takes piece blockIdx.x % (ry * rx) of it, the
+// tile cut into ry row bands and rx column bands (ry = rx = 1: the whole
+// tile).  Pieces serve the last, partly filled round of a launch.
 struct TileMap {
   int gx;
   int first;
-  int sub;
+  int ry;
+  int rx;
 };
 
 __device__ __forceinline__ void map_tile(const TileMap& tm, int& bx, int& by) {
-  if (tm.sub == 0) {
-    const int t = tm.first + (int)blockIdx.x;
-    bx = t % tm.gx;
-    by = t / tm.gx;
-  } else if (tm.sub == 1) {
-    const int t = tm.first + (int)(blockIdx.x >> 1), q = (int)(blockIdx.x & 1);
-    bx = t % tm.gx;
-    by = (t / tm.gx) * 2 + q;
-  } else {
-    const int t = tm.first + (int)(blockIdx.x >> 2), q = (int)(blockIdx.x & 3);
-    bx = (t % tm.gx) * 2 + (q & 1);
-    by = (t / tm.gx) * 2 + (q >> 1);
-  }
+  const int per = tm.ry * tm.rx;
+  const int t = tm.first + (int)blockIdx.x / per, q = (int)blockIdx.x % per;
+  bx = (t % tm.gx) * tm.rx + q % tm.rx;
+  by = (t / tm.gx) * tm.ry + q / tm.rx;
 }
 
 template <int MF, int NF, int WM, int WN, int NSTAGE>
@@ -821,9 +811,10 @@ if constexpr (PIPE) {
 
   // Sub-step 3 follows the LDS reads of the next stage: its first MFMAs go out
   // before any VALU op that needs the new fragments.
+  constexpr int LATE = NVFP4_LATE < MF * NF ? NVFP4_LATE : MF * NF;
   auto interleave_late = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x008, NVFP4_LATE, 0);
-    static_for<0, MF * NF - NVFP4_LATE>([&](auto) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x008, LATE, 0);
+    static_for<0, MF * NF - LATE>([&](auto) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_XPIPE + 1, 0);
     });
@@ -1474,36 +1465,45 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
   dim3 block(WM * WN * 64);
   if ((k & 63) == 0 && k / kTileK >= NS) {
     // One workgroup per CU at a time: when the last round would leave most
-    // CUs idle, its tiles run as a second launch of quarter-size (four per
-    // tile) or half-height (two per tile) workgroups -- whichever still fits
-    // one round -- which fills the machine and finishes that round sooner.
-    // (SiLU*mul tiles are only halved: a quarter would split gate from up.)
+    // CUs idle, its tiles run as a second launch of smaller pieces -- each
+    // tile cut into ry row bands and rx column bands, the finest cut whose
+    // pieces still fit one round -- which fills the machine and finishes that
+    // round sooner.  (SiLU*mul tiles are only cut into row bands: a column
+    // cut would split gate from up.)
     const int64_t tiles = (int64_t)grid.x * grid.y, cus = cu_count(), rem = tiles % cus;
-    int split = 0;
+    int ry = 1, rx = 1;
     if (tiles > cus && rem > 0) {
-      if (!epi.silu_mul && rem * 4 <= cus) split = 2;
-      else if (rem * 2 <= cus) split = 1;
+      static const int cuts[4][2] = {{4, 4}, {4, 2}, {2, 2}, {2, 1}};
+      static const int silu_cuts[2][2] = {{4, 1}, {2, 1}};
+      const int (*c)[2] = epi.silu_mul ? silu_cuts : cuts;
+      const int nc = epi.silu_mul ? 2 : 4;
+      for (int i = 0; i < nc; ++i)
+        if (rem * c[i][0] * c[i][1] <= cus) {
+          ry = c[i][0];
+          rx = c[i][1];
+          break;
+        }
     }
-    const int64_t nbig = split ? tiles - rem : tiles;
-    const TileMap big{(int)grid.x, 0, 0};
-    const TileMap tail{(int)grid.x, (int)nbig, split};
-    const dim3 tail_grid((unsigned)(rem * (split == 2 ? 4 : 2)));
+    const bool cut = ry * rx > 1;
+    const int64_t nbig = cut ? tiles - rem : tiles;
+    const TileMap big{(int)grid.x, 0, 1, 1};
+    const TileMap tail{(int)grid.x, (int)nbig, ry, rx};
+    const dim3 tail_grid((unsigned)(rem * ry * rx));
+#define NVFP4_LAUNCH_PIECE(MFP, NFP, SL, GRID, MAP) \
+  hipLaunchKernelGGL((gemm_prefill_dma_kernel<MFP, NFP, WM, WN, NS, SL, true>), GRID, block, 0, st, ac, as, m, w, n, \
+                     k, out, epi, MAP)
     if (epi.silu_mul) {
-      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, true, true>), dim3((unsigned)nbig), block, 0, st,
-                         ac, as, m, w, n, k, out, epi, big);
-      if (split == 1)
-        hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF / 2, NF, WM, WN, NS, true, true>), tail_grid, block, 0, st,
-                           ac, as, m, w, n, k, out, epi, tail);
+      NVFP4_LAUNCH_PIECE(MF, NF, true, dim3((unsigned)nbig), big);
+      if (ry == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF, true, tail_grid, tail);
+      if (ry == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF, true, tail_grid, tail);
     } else {
-      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF, NF, WM, WN, NS, false, true>), dim3((unsigned)nbig), block, 0,
-                         st, ac, as, m, w, n, k, out, epi, big);
-      if (split == 1)
-        hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF / 2, NF, WM, WN, NS, false, true>), tail_grid, block, 0, st,
-                           ac, as, m, w, n, k, out, epi, tail);
-      if (split == 2)
-        hipLaunchKernelGGL((gemm_prefill_dma_kernel<MF / 2, NF / 2, WM, WN, NS, false, true>), tail_grid, block, 0,
-                           st, ac, as, m, w, n, k, out, epi, tail);
+      NVFP4_LAUNCH_PIECE(MF, NF, false, dim3((unsigned)nbig), big);
+      if (ry == 2 && rx == 1) NVFP4_LAUNCH_PIECE(MF / 2, NF, false, tail_grid, tail);
+      if (ry == 2 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF / 2, false, tail_grid, tail);
+      if (ry == 4 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 4, NF / 2, false, tail_grid, tail);
+      if (ry == 4 && rx == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF / 4, false, tail_grid, tail);
     }
+#undef NVFP4_LAUNCH_PIECE
   } else {
     if (epi.silu_mul)
       hipLaunchKernelGGL((gemm_prefill_regs_kernel<MF, NF, WM, WN, true>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);

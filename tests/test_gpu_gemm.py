@@ -74,8 +74,11 @@ def test_unit_scales_give_the_exact_integer_product(gpu_lib):
     (37, 96, 5120, "f32"),       # decode kernel, long K
     (1, 33, 32, "f32"),          # smallest K
     (512, 256, 1024, "bf16"),
-    (512, 33184, 256, "bf16"),   # 260 tiles of 256x256: on 256 CUs the last 4 run as quarter tiles; ragged N
-    (512, 46040, 256, "f32"),    # 360 tiles: the last 104 run as half-height tiles; ragged N
+    # last-round cuts on 256 CUs (tiles of 256x256, two row blocks at M=512):
+    (512, 33184, 256, "bf16"),   # 260 tiles: the last 4 run as 16 pieces of 64x64 each; ragged N
+    (512, 35712, 256, "f32"),    # 280 tiles: the last 24 as 8 pieces of 64x128
+    (512, 38336, 256, "bf16"),   # 300 tiles: the last 44 as quarters (128x128)
+    (512, 46040, 256, "f32"),    # 360 tiles: the last 104 as half-height tiles; ragged N
 ])
 def test_gemm_matches_oracle_everywhere(gpu_lib, M, N, K, out):
     rng = np.random.default_rng(M * 1000003 + N * 101 + K)
@@ -247,7 +250,8 @@ def test_fused_segments_small(gpu_lib, M):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 192, 256), (40, 192, 256), (130, 192, 256),
-                                   (512, 256, 38400)])   # 300 gate/up tiles: the last 44 run as half tiles
+                                   (512, 256, 38400),    # 300 gate/up tiles: the last 44 as 4 row bands each
+                                   (512, 256, 43520)])   # 340 tiles: the last 84 as half-height tiles
 def test_silu_mul_small(gpu_lib, M, K, N):
     rng = np.random.default_rng(100 + M)
     a = rng.standard_t(4, size=(M, K)).astype(np.float32)
