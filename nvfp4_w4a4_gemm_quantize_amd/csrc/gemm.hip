@@ -1137,7 +1137,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 }
 
 // ------------------------------------------------ decode kernel, FP4 MFMA ----
-// m <= 8: weight streaming on gfx950's block-scaled FP4 MFMA, applied to the
+// m <= 4: weight streaming on gfx950's block-scaled FP4 MFMA, applied to the
 // raw E2M1 codes (no dequantisation).  The packed weight tile is already the
 // B operand of v_mfma_scale_f32_32x32x64_f8f6f4 (lane r + 32h: column r, K
 // 32h..32h+31).  The A operand puts each 16-element block of each A row in a
