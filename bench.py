@@ -383,6 +383,32 @@ def gdn_repairs(torch, B, S, reps=5):
     return out
 
 
+def bf16_library_context(torch, reps=5):
+    """Context, not part of the path: the same three prefill GEMMs as plain bf16 matrix products through
+    torch (hipBLASLt), unquantised operands -- a measured practical MFMA ceiling on this GPU.  Two-
+    dimensional products only (no batched kernels)."""
+    import torch.nn.functional as F
+    out = {}
+    for name, (n, k) in (("gdn", (16480, 5120)), ("gate_up", (34816, 5120)), ("down", (5120, 17408))):
+        a = torch.randn((4096, k), device="cuda").to(torch.bfloat16)
+        w = (torch.randn((n, k), device="cuda") * k ** -0.5).to(torch.bfloat16)
+        F.linear(a, w)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            F.linear(a, w)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[name] = {"us": round(us, 1), "tflops": round(2 * 4096 * n * k / us / 1e6, 1)}
+        del a, w
+    torch.cuda.empty_cache()
+    tot = sum(FLOP[x] for x in ("gdn", "gate_up", "down")) / sum(out[x]["us"] for x in out) / 1e6
+    out["all_3_tflops"] = round(tot, 1)
+    return out
+
+
 REC_FLOP_PER_HEAD_TOKEN = 7 * 128 * 128      # two 128x128 dot passes (2 d^2 each) + decay-and-write (3 d^2)
 PEAK_F32_VECTOR_TFLOPS = 157.3                # MI355X fp32 vector (packed); 78.6 without packed FP32
 
@@ -451,7 +477,8 @@ def main():
     fused_mlp = mlp_fused(torch, B, S)
     repairs = gdn_repairs(torch, B, S)
     recurrence = gdn_recurrence_run(torch, B, S)
-    progress("fused MLP, GDN repairs and the recurrence timed")
+    bf16_ctx = bf16_library_context(torch)
+    progress("fused MLP, GDN repairs, the recurrence and the bf16 library context timed")
     traffic = measured_traffic()
     progress("decode sweep done")
     if args.copy_probe_mib > 0:
@@ -499,6 +526,7 @@ def main():
         "mlp_fused_h_quantize": fused_mlp,
         "gdn_scale_repairs": repairs,
         "gdn_recurrence": recurrence,
+        "bf16_torch_linear_context": bf16_ctx,
         "setup_s": round(S["setup_s"], 1),
     }
     if not args.no_cpu_baseline:
