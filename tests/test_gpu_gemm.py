@@ -73,6 +73,8 @@ def test_unit_scales_give_the_exact_integer_product(gpu_lib):
     (65, 160, 64, "bf16"),       # just above the decode limit, a single K tile
     (37, 96, 5120, "f32"),       # decode kernel, long K
     (1, 33, 32, "f32"),          # smallest K
+    (7, 1000, 5120, "bf16"),     # f16 decode kernel just above the FP4 path's rows, ragged N
+    (5, 64, 320, "f32"),         # f16 decode kernel, a K of 1.25 weight super-tiles
     (512, 256, 1024, "bf16"),
     # last-round cuts on 256 CUs (tiles of 256x256, two row blocks at M=512):
     (512, 33184, 256, "bf16"),   # 260 tiles: the last 4 run as 16 pieces of 64x64 each; ragged N
