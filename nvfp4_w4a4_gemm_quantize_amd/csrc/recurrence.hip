@@ -173,8 +173,9 @@ gdn_recurrence_kernel(GdnArgs a) {
     if (c + 1 < nchunks) load(c + 1, R);
     const Stage& S = st[c & 1];
     const int cnt = (int)(T - c * kChunk < kChunk ? T - c * kChunk : kChunk);
-#pragma unroll 2
-    for (int step = 0; step < cnt; ++step) {
+    // One time step for this lane's eight state elements.  Every lane of a
+    // row holds the row's output (identical bits), so all of them write it.
+    auto step_fn = [&](int step) __attribute__((always_inline)) {
       const float4 ka = reinterpret_cast<const float4*>(S.kn[step])[lr];
       const float4 kb = reinterpret_cast<const float4*>(S.kn[step])[16 + lr];
       const float4 qa = reinterpret_cast<const float4*>(S.qn[step])[lr];
@@ -195,7 +196,15 @@ gdn_recurrence_kernel(GdnArgs a) {
       const float kv[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) s[j] = fmaf(alpha, s[j], cw * kv[j]);
-      if (lr == 0) obuf[step][rloc] = o;
+      obuf[step][rloc] = o;
+    };
+    // Full chunks: the step loop unrolled (LDS offsets become immediates, no
+    // loop-carried register copies); the last, partial chunk: a plain loop.
+    if (cnt == kChunk) {
+#pragma unroll
+      for (int step = 0; step < kChunk; ++step) step_fn(step);
+    } else {
+      for (int step = 0; step < cnt; ++step) step_fn(step);
     }
     __syncthreads();
     if (c + 1 < nchunks) store(R, st[(c + 1) & 1]);
