@@ -9,8 +9,19 @@
 //     u = alpha S k^,  c = beta (v - u),  S <- alpha S + c k^T,  o = S q^.
 // Since the dot products are taken on the state before the step,
 //     u_i = alpha (S_i . k^),  o_i = alpha (S_i . q^) + c_i (k^ . q^),
-// both dots of a row come from one pass over the old state, and the update is
-// one multiply-add per element.
+// both dots of a row come from one pass over the old state.
+//
+// Scaled state: within a segment of 8 steps the registers hold S^ = S / A,
+// A = the product of the segment's decays so far, so that a step is
+//     u = A (S^ . k^),  c = beta (v - u),  o = A (S^ . q^) + c (k^ . q^),
+//     S^ <- S^ + (c / A) k^,
+// one multiply-add per element instead of a multiply and a multiply-add; at
+// the segment's end S = A S^ is restored.  Floating point being scale-free,
+// this changes only which products are rounded: the state's effective decay
+// per step is the ratio of two consecutive rounded A, within a few units of
+// roundoff of alpha.  A chunk whose decays all lie in [2^-12, 2^12] keeps A
+// and 1 / A within [2^-96, 2^96]; any other chunk (a near-total reset, a
+// growing gate, NaN) runs the unscaled update.
 //
 // Work split: the recurrence is sequential in time and independent per state
 // row, so a workgroup owns 16 rows of one head's state in registers for the
@@ -21,8 +32,13 @@
 // a time through double-buffered LDS: while a chunk is being consumed the
 // next one is loaded into registers, then converted -- keys and queries to
 // normalised fp32 (their norms reduced once per step per workgroup), gates to
-// (alpha, beta, k^.q^) -- and written to the other buffer.  ALU-bound: about
-// 7 * 128^2 flops per head per token.
+// (alpha, beta, k^.q^, A, 1/A) -- and written to the other buffer; within a
+// chunk each step's LDS operands are read during the step before.  ALU-bound:
+// about 7 * 128^2 flops per head per token.  (Layouts with one wave per SIMD
+// -- 8 lanes x 16 columns per row, or two rows per lane -- balance the SIMDs
+// at 48 heads but issue less well from a lone wave and measured slower.)
+#include <type_traits>
+
 #include "kernels.h"
 #include "nvfp4_device.h"
 
@@ -34,6 +50,9 @@ constexpr int kD = 128;          // key and value dimension of a head
 constexpr int kRows = 16;        // state rows per workgroup
 constexpr int kThreads = 256;    // 4 waves x 4 rows x 16 lanes
 constexpr int kChunk = 32;       // time steps per LDS stage
+constexpr int kSeg = 8;          // time steps per segment of the scaled state
+static_assert(kChunk % kSeg == 0 && (kSeg & (kSeg - 1)) == 0, "segments tile a chunk");
+static_assert(kThreads == 16 * kRows && kChunk == 2 * (kThreads / 16), "a chunk's outputs are two steps per thread");
 constexpr float kNormEps = 1e-6f;
 
 struct Stage {
@@ -41,6 +60,8 @@ struct Stage {
   float qn[kChunk][kD];     // normalised queries
   float v[kChunk][kRows];   // this workgroup's value rows
   float4 sc[kChunk];        // alpha, beta, k^ . q^, unused
+  float2 sa[kChunk];        // A (decay product since the step's 8-step segment began), 1 / A
+  int scaled;               // every decay of the chunk within [2^-12, 2^12]
 };
 
 __device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -70,7 +91,7 @@ struct Raw {
 
 }  // namespace
 
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gdn_recurrence_kernel(GdnArgs a) {
   __shared__ Stage st[2];
   __shared__ float obuf[kChunk][kRows];
@@ -96,8 +117,28 @@ gdn_recurrence_kernel(GdnArgs a) {
     for (int j = 0; j < 8; ++j) s[j] = 0.0f;
   }
 
+  // Loop-invariant parts of this thread's element offsets; a chunk adds its
+  // first step times the leading dimension (a workgroup-uniform value).
+  const int64_t koff = (int64_t)(t >> 4) * a.ld_k + hk * kD + 8 * (t & 15);
+  const int64_t qoff = (int64_t)(t >> 4) * a.ld_q + hk * kD + 8 * (t & 15);
+  const int64_t voff = (int64_t)(t >> 1) * a.ld_v + (int64_t)h * kD + i0 + 8 * (t & 1);
+  const int64_t boff = (int64_t)t * a.ld_beta + h, goff = (int64_t)t * a.ld_g + h;
   auto load = [&](int64_t chunk, Raw& R) __attribute__((always_inline)) {
     const int64_t t0 = chunk * kChunk;
+    if (t0 + kChunk <= T) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        R.k[p] = *reinterpret_cast<const uint4*>(a.k + (t0 + 16 * p) * a.ld_k + koff);
+        R.q[p] = *reinterpret_cast<const uint4*>(a.q + (t0 + 16 * p) * a.ld_q + qoff);
+      }
+      if (t < 2 * kChunk) R.v = *reinterpret_cast<const uint4*>(a.v + t0 * a.ld_v + voff);
+      if (t < kChunk) {
+        R.beta = a.beta[t0 * a.ld_beta + boff];
+        R.g = a.g[t0 * a.ld_g + goff];
+      }
+      return;
+    }
+    // the last, partial chunk: steps past the end read the last step again
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       int64_t step = t0 + p * 16 + (t >> 4);
@@ -143,7 +184,8 @@ gdn_recurrence_kernel(GdnArgs a) {
       kk = row_sum16(kk);
       qq = row_sum16(qq);
       kq = row_sum16(kq);
-      const float nk = 1.0f / sqrtf(kk + kNormEps), nq = 1.0f / sqrtf(qq + kNormEps);
+      // hardware reciprocal square root (within 1 ulp; the sums are >= eps, normal)
+      const float nk = __builtin_amdgcn_rsqf(kk + kNormEps), nq = __builtin_amdgcn_rsqf(qq + kNormEps);
       float4* kd = reinterpret_cast<float4*>(&S.kn[step][8 * pc]);
       float4* qd = reinterpret_cast<float4*>(&S.qn[step][8 * pc]);
       kd[0] = make_float4(kf[0] * nk, kf[1] * nk, kf[2] * nk, kf[3] * nk);
@@ -160,11 +202,24 @@ gdn_recurrence_kernel(GdnArgs a) {
       vd[1] = make_float4(vf[4], vf[5], vf[6], vf[7]);
     }
     if (t < kChunk) {
-      S.sc[t].x = expf(bf16f(R.g & 0xFFFFu));
+      const float alpha = expf(bf16f(R.g & 0xFFFFu));
+      S.sc[t].x = alpha;
       S.sc[t].y = bf16f(R.beta & 0xFFFFu);
+      // product of the decays from the segment's first step to this one
+      float A = alpha;
+#pragma unroll
+      for (int off = 1; off < kSeg; off <<= 1) {
+        const float y = __shfl_up(A, off, kSeg);
+        if ((t & (kSeg - 1)) >= off) A *= y;
+      }
+      S.sa[t] = make_float2(A, __builtin_amdgcn_rcpf(A));      // within 1 ulp
+      const bool in_range = alpha >= 0x1p-12f && alpha <= 0x1p12f;    // false for NaN
+      const uint64_t out = __ballot(!in_range);
+      if (t == 0) S.scaled = out == 0;
     }
   };
 
+  const int64_t ooff = (int64_t)(t >> 4) * a.ld_o + (int64_t)h * kD + i0 + (t & 15);
   Raw R;
   load(0, R);
   store(R, st[0]);
@@ -173,15 +228,25 @@ gdn_recurrence_kernel(GdnArgs a) {
     if (c + 1 < nchunks) load(c + 1, R);
     const Stage& S = st[c & 1];
     const int cnt = (int)(T - c * kChunk < kChunk ? T - c * kChunk : kChunk);
-    // One time step for this lane's eight state elements.  Every lane of a
-    // row holds the row's output (identical bits), so all of them write it.
-    auto step_fn = [&](int step) __attribute__((always_inline)) {
-      const float4 ka = reinterpret_cast<const float4*>(S.kn[step])[lr];
-      const float4 kb = reinterpret_cast<const float4*>(S.kn[step])[16 + lr];
-      const float4 qa = reinterpret_cast<const float4*>(S.qn[step])[lr];
-      const float4 qb = reinterpret_cast<const float4*>(S.qn[step])[16 + lr];
-      const float4 sc = S.sc[step];
-      const float vi = S.v[step][rloc];
+    // One time step for this lane's eight state elements, scaled (S^ = S / A)
+    // or not.  Every lane of a row holds the row's output (identical bits), so
+    // all of them write it.
+    struct In { float4 ka, kb, qa, qb, sc; float2 sa; float vi; };
+    auto fetch = [&](int step) __attribute__((always_inline)) {
+      In x;
+      x.ka = reinterpret_cast<const float4*>(S.kn[step])[lr];
+      x.kb = reinterpret_cast<const float4*>(S.kn[step])[16 + lr];
+      x.qa = reinterpret_cast<const float4*>(S.qn[step])[lr];
+      x.qb = reinterpret_cast<const float4*>(S.qn[step])[16 + lr];
+      x.sc = S.sc[step];
+      x.sa = S.sa[step];
+      x.vi = S.v[step][rloc];
+      return x;
+    };
+    auto compute = [&](int step, const In& x, auto scaled_tag) __attribute__((always_inline)) {
+      constexpr bool kScaled = decltype(scaled_tag)::value;
+      const float4 ka = x.ka, kb = x.kb, qa = x.qa, qb = x.qb, sc = x.sc;
+      const float vi = x.vi;
       float sk0 = s[0] * ka.x, sk1 = s[1] * ka.y, sq0 = s[0] * qa.x, sq1 = s[1] * qa.y;
       sk0 = fmaf(s[2], ka.z, sk0); sk1 = fmaf(s[3], ka.w, sk1);
       sq0 = fmaf(s[2], qa.z, sq0); sq1 = fmaf(s[3], qa.w, sq1);
@@ -190,30 +255,54 @@ gdn_recurrence_kernel(GdnArgs a) {
       sk0 = fmaf(s[6], kb.z, sk0); sk1 = fmaf(s[7], kb.w, sk1);
       sq0 = fmaf(s[6], qb.z, sq0); sq1 = fmaf(s[7], qb.w, sq1);
       const float sk = row_sum16(sk0 + sk1), sq = row_sum16(sq0 + sq1);
-      const float alpha = sc.x, beta = sc.y;
-      const float cw = beta * (vi - alpha * sk);
-      const float o = fmaf(alpha, sq, cw * sc.z);
       const float kv[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+      const float beta = sc.y;
+      if constexpr (kScaled) {
+        const float2 sa = x.sa;
+        const float cw = beta * (vi - sa.x * sk);
+        obuf[step][rloc] = fmaf(sa.x, sq, cw * sc.z);
+        const float d = cw * sa.y;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] = fmaf(alpha, s[j], cw * kv[j]);
-      obuf[step][rloc] = o;
+        for (int j = 0; j < 8; ++j) s[j] = fmaf(d, kv[j], s[j]);
+        if ((step & (kSeg - 1)) == kSeg - 1) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s[j] *= sa.x;
+        }
+      } else {
+        const float alpha = sc.x;
+        const float cw = beta * (vi - alpha * sk);
+        obuf[step][rloc] = fmaf(alpha, sq, cw * sc.z);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] = fmaf(alpha, s[j], cw * kv[j]);
+      }
     };
-    // Full chunks: the step loop unrolled (LDS offsets become immediates, no
-    // loop-carried register copies); the last, partial chunk: a plain loop.
-    if (cnt == kChunk) {
+    auto run_full = [&](auto scaled_tag) __attribute__((always_inline)) {
+      In cur = fetch(0);
 #pragma unroll
-      for (int step = 0; step < kChunk; ++step) step_fn(step);
+      for (int step = 0; step < kChunk; ++step) {
+        In nxt;
+        if (step + 1 < kChunk) nxt = fetch(step + 1);
+        asm volatile("" ::: "memory");
+        compute(step, cur, scaled_tag);
+        cur = nxt;
+      }
+    };
+    if (cnt == kChunk && __builtin_amdgcn_readfirstlane(S.scaled)) {
+      run_full(std::true_type{});
+    } else if (cnt == kChunk) {
+      run_full(std::false_type{});
     } else {
-      for (int step = 0; step < cnt; ++step) step_fn(step);
+      for (int step = 0; step < cnt; ++step) compute(step, fetch(step), std::false_type{});
     }
     __syncthreads();
     if (c + 1 < nchunks) store(R, st[(c + 1) & 1]);
-    // this chunk's outputs: kChunk x 16 values, two per thread
+    // this chunk's outputs: kChunk x 16 values, two per thread (steps
+    // t/16 and 16 + t/16, row t%16)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int idx = t + e * kThreads, step = idx >> 4, r = idx & 15;
+      const int step = (t >> 4) + 16 * e, r = t & 15;
       if (step < cnt) {
-        const int64_t off = (c * kChunk + step) * a.ld_o + (int64_t)h * kD + i0 + r;
+        const int64_t off = (c * kChunk + 16 * e) * a.ld_o + ooff;
         const float val = obuf[step][r];
         if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[off] = f32_to_bf16_rne(val);
         else reinterpret_cast<float*>(a.o)[off] = val;

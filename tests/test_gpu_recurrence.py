@@ -46,14 +46,29 @@ def gpu_run(lib, d, hk, hv, s_init=None, out_dtype=torch.float32):
                               return_state=True, out_dtype=out_dtype)
 
 
-@pytest.mark.parametrize("T,hk,hv,with_init,bf16_out", [
-    (300, 2, 6, True, False),     # ragged last chunk, grouped key heads, initial state
-    (1, 1, 1, False, False),      # a single step
-    (32, 1, 2, True, True),       # exactly one chunk; bf16 output
-    (33, 4, 4, False, False),     # one step into the second chunk
+def _with_resets(d, seed):
+    """Near-total resets (g = -12, decay 6e-6) at 2% of the steps: about half of
+    the 32-step chunks hold one, so both the scaled and the unscaled state
+    update run, in every head, with switches between them."""
+    g = f(d["g"])
+    hit = np.random.default_rng(seed).uniform(size=g.shape) < 0.02
+    out = dict(d)
+    out["g"] = inputs.f32_to_bf16_bits(np.where(hit, -12.0, g).astype(np.float32))
+    return out
+
+
+@pytest.mark.parametrize("T,hk,hv,with_init,bf16_out,resets", [
+    (300, 2, 6, True, False, False),     # ragged last chunk, grouped key heads, initial state
+    (1, 1, 1, False, False, False),      # a single step
+    (32, 1, 2, True, True, False),       # exactly one chunk; bf16 output
+    (33, 4, 4, False, False, False),     # one step into the second chunk
+    (640, 2, 6, True, False, True),      # decays outside [2^-12, 2^12] in some chunks
+    (301, 1, 3, False, True, True),
 ])
-def test_recurrence_parity_small(gpu_lib, T, hk, hv, with_init, bf16_out):
+def test_recurrence_parity_small(gpu_lib, T, hk, hv, with_init, bf16_out, resets):
     d = inputs.recurrence(T, hk, hv, seed=T)
+    if resets:
+        d = _with_resets(d, T + 1)
     s0 = (np.random.default_rng(T).standard_normal((hv, D, D)) * 0.05).astype(np.float32) if with_init else None
     o, S = gpu_run(gpu_lib, d, hk, hv, s0, torch.bfloat16 if bf16_out else torch.float32)
     o_ref, S_ref, l1 = oracle_run(d, hk, hv, s0)
