@@ -7,8 +7,9 @@ Parity: every output element within the fp32 bound of
 row magnitude, accumulated over the steps, never amplified because each step
 is non-expansive), the final state likewise, ragged chunk tails, one step,
 grouped key heads, strided inputs inside a fused in-projection buffer, an
-initial state, bf16 output, run-to-run identity; at the full head layout
-(16 key / 48 value heads) over 4096 tokens.
+initial state, bf16 output, run-to-run identity, near-total resets in some
+chunks (which run the unscaled state update while the rest run the scaled
+one); at the full head layout (16 key / 48 value heads) over 4096 tokens.
 Mechanism: noise of 10% injected into keys, values and both gates at every
 step leaves the output error at a flat plateau over 32768 tokens; a random
 state impulse (values zero) is forgotten, its output falling by 100x within
