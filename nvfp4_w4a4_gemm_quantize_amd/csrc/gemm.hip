@@ -933,8 +933,13 @@ if constexpr (PIPE) {
 // ALDS (small m*k): the workgroup first dequantises A once into LDS as f16 in
 // MFMA operand order (rows < m only; lanes of absent rows read a zero slot),
 // so the loop spends VALU only on the weights.  Otherwise A is dequantised
-// per tile in registers.  The waves' partial accumulators are summed in LDS in
-// a fixed order.
+// per tile in registers.  GA (k % 256 == 0, 16-byte aligned A scales): A is
+// fetched four K tiles at a time, eight lanes per 128-byte row segment, and
+// each wave re-orders its group through a private LDS area into MFMA lane
+// order -- a per-tile fetch in lane order would touch one cache line per row
+// per instruction, and at 32 or 64 rows those line lookups, not the bytes,
+// limit the kernel.  The waves' partial accumulators are summed in LDS in a
+// fixed order.
 constexpr int kDecodeALdsBytes = 48 * 1024;
 #ifndef NVFP4_DECODE_GROUP_A
 #define NVFP4_DECODE_GROUP_A 6
@@ -947,14 +952,19 @@ constexpr int kDecodeGroupA = NVFP4_DECODE_GROUP_A;
 // A staging in dynamic LDS of exactly (m+1)*k*2 bytes): the 544 workgroups of
 // a 17408-column projection are then all resident at once instead of the
 // last few running as a second round.
-template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U>
+constexpr int kDecodeGroupRow = 144;          // LDS bytes per A row of a group (128 + 16: conflict-free reads)
+constexpr int kDecodeGroupFrag = 32 * kDecodeGroupRow;
+
+template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U, bool GA>
 __global__ void __launch_bounds__(DW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
                    const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
                    EpilogueArgs epi) {
   constexpr int NS = SILU ? 2 : 1;                 // weight slabs per workgroup
   constexpr int NACC = MFD * NS;
+  static_assert(!GA || (!ALDS && U == 4), "grouped A fetch: four tiles per load group");
   __shared__ float s_red[DW - 1][NACC][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ag[GA ? DW * MFD * kDecodeGroupFrag : 16];
   extern __shared__ __attribute__((aligned(16))) uint8_t s_a[];    // ALDS: (m+1)*k*2 bytes
 
   const int t = threadIdx.x;
@@ -966,7 +976,9 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   int64_t slab[NS];
   slab[0] = blockIdx.x;
   if (SILU) slab[NS - 1] = blockIdx.x + (n / 2) / kTileN;
-  const int64_t kt0 = KT * wave / DW, kt1 = KT * (wave + 1) / DW;
+  // GA: wave ranges in whole groups of four tiles (KT % 4 == 0 there)
+  const int64_t kt0 = GA ? (KT / 4) * wave / DW * 4 : KT * wave / DW;
+  const int64_t kt1 = GA ? (KT / 4) * (wave + 1) / DW * 4 : KT * (wave + 1) / DW;
 
   // Independent accumulators per K sub-step break the MFMA dependency chain
   // (a single 32x32 output tile would otherwise serialise every MFMA).
@@ -988,13 +1000,14 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   const int64_t a_rows = m + 1;
   const uint32_t a_lane = (uint32_t)((h * a_rows + (r < m ? r : m)) * 16);
 
-  struct Tile { uint4 a[ALDS ? 1 : MFD]; uint32_t as[ALDS ? 1 : MFD]; uint4 b[NS]; uint32_t bs[NS]; };
+  constexpr bool ATILE = !ALDS && !GA;             // A fetched per tile in lane order
+  struct Tile { uint4 a[ATILE ? MFD : 1]; uint32_t as[ATILE ? MFD : 1]; uint4 b[NS]; uint32_t bs[NS]; };
   // Loads are unconditional (no branches, so the compiler can count them and
   // wait only for the group about to be multiplied); tiles past the wave's
   // range are clamped to its last tile and never multiplied.
   auto load = [&](int64_t kt, Tile& T) __attribute__((always_inline)) {
     kt = kt < kt1 ? kt : kt1 - 1;
-    if constexpr (!ALDS) {
+    if constexpr (ATILE) {
 #pragma unroll
       for (int i = 0; i < MFD; ++i) {
         const int64_t row = i * 32 + r;
@@ -1009,7 +1022,10 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
       T.bs[j] = *reinterpret_cast<const uint16_t*>(w_packed + tile_scale_off(slab[j], kt, KS, 0) + ws_lane);
     }
   };
-  auto compute = [&](int64_t kt, const Tile& T) __attribute__((always_inline)) {
+  // A of one tile for the non-ALDS paths: codes (16 bytes: K half h of row
+  // i*32 + r) and the scale pair of those two blocks.
+  struct ATileRegs { uint4 a[MFD]; uint32_t as[MFD]; };
+  auto compute = [&](int64_t kt, const Tile& T, const ATileRegs& A) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       half8_t av[MFD], bv[NS];
@@ -1019,8 +1035,8 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
       } else {
 #pragma unroll
         for (int i = 0; i < MFD; ++i) {
-          const uint32_t cw = s == 0 ? T.a[i].x : s == 1 ? T.a[i].y : s == 2 ? T.a[i].z : T.a[i].w;
-          av[i] = dequant8(cw, scale_pair_f16(scale_byte(T.as[i], s)));
+          const uint32_t cw = s == 0 ? A.a[i].x : s == 1 ? A.a[i].y : s == 2 ? A.a[i].z : A.a[i].w;
+          av[i] = dequant8(cw, scale_pair_f16(scale_byte(A.as[i], s)));
         }
       }
 #pragma unroll
@@ -1034,20 +1050,71 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
         for (int j = 0; j < NS; ++j) part[i][j][s % NSUB] = mfma32x32x16(av[i], bv[j], part[i][j][s % NSUB]);
     }
   };
-  auto load_group = [&](int64_t g0, Tile (&T)[U]) __attribute__((always_inline)) {
+  // GA: one group's A -- codes of rows i*32 + 8j + lane/8, 16-byte segment
+  // lane%8 of the group's 128 bytes per row, and each lane's row i*32 + r's
+  // scales for the group's four tiles (16 bytes).
+  struct AGroup { uint4 c[GA ? MFD : 1][GA ? 4 : 1]; uint4 s[GA ? MFD : 1]; };
+  uint8_t* const ag_base = s_ag + (GA ? wave * MFD * kDecodeGroupFrag : 0);
+  auto load_agroup = [&](int64_t g0, AGroup& G) __attribute__((always_inline)) {
+    if constexpr (GA) {
+      g0 = g0 < kt1 - 4 ? g0 : kt1 - 4;              // groups past the wave's range: never multiplied
+#pragma unroll
+      for (int i = 0; i < MFD; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t row = i * 32 + 8 * j + (lane >> 3);
+          G.c[i][j] = ld16(a_codes + row * a_row_bytes + g0 * 32 + (lane & 7) * 16, row < m);
+        }
+        const int64_t row = i * 32 + r;
+        G.s[i] = ld16(a_scales + row * a_row_scales + g0 * 4, row < m);
+      }
+    }
+  };
+  auto load_group = [&](int64_t g0, Tile (&T)[U], AGroup& G) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) load(g0 + u, T[u]);
+    load_agroup(g0, G);
   };
-  auto compute_group = [&](int64_t g0, const Tile (&T)[U]) __attribute__((always_inline)) {
+  auto compute_group = [&](int64_t g0, const Tile (&T)[U], const AGroup& G) __attribute__((always_inline)) {
+    if constexpr (GA) {
+      // this wave's group through its LDS area into lane order (the previous
+      // group's reads were issued before these writes)
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (g0 + u < kt1) compute(g0 + u, T[u]);
+      for (int i = 0; i < MFD; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint4*>(ag_base + i * kDecodeGroupFrag + (8 * j + (lane >> 3)) * kDecodeGroupRow +
+                                    (lane & 7) * 16) = G.c[i][j];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u < kt1) {
+        ATileRegs A;
+        if constexpr (GA) {
+#pragma unroll
+          for (int i = 0; i < MFD; ++i) {
+            A.a[i] = *reinterpret_cast<const uint4*>(ag_base + i * kDecodeGroupFrag + r * kDecodeGroupRow +
+                                                     (2 * u + h) * 16);
+            const uint32_t w = u == 0 ? G.s[i].x : u == 1 ? G.s[i].y : u == 2 ? G.s[i].z : G.s[i].w;
+            A.as[i] = (w >> (16 * h)) & 0xFFFFu;
+          }
+        } else if constexpr (ATILE) {
+#pragma unroll
+          for (int i = 0; i < MFD; ++i) {
+            A.a[i] = T[u].a[i];
+            A.as[i] = T[u].as[i];
+          }
+        }
+        compute(g0 + u, T[u], A);
+      }
+    }
   };
 
   // The first weight group is requested before A is staged, so its latency
   // overlaps the staging.
   Tile g_a[U], g_b[U];
-  if (kt0 < kt1) load_group(kt0, g_a);
+  AGroup ag_a, ag_b;
+  if (kt0 < kt1) load_group(kt0, g_a, ag_a);
   // Stage A into LDS once per workgroup (ALDS): dequantised f16 chunks in MFMA
   // operand order plus one zero row per (kt, s, hh) group.
   if constexpr (ALDS) {
@@ -1072,10 +1139,10 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 
   if (kt0 < kt1) {
     for (int64_t g = kt0; g < kt1; g += 2 * U) {
-      load_group(g + U, g_b);
-      compute_group(g, g_a);
-      load_group(g + 2 * U, g_a);
-      compute_group(g + U, g_b);
+      load_group(g + U, g_b, ag_b);
+      compute_group(g, g_a, ag_a);
+      load_group(g + 2 * U, g_a, ag_a);
+      compute_group(g + U, g_b, ag_b);
     }
   }
 
@@ -1520,8 +1587,17 @@ static void launch_decode_kernel(const uint8_t* ac, const uint8_t* as, int64_t m
                                  int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
   const unsigned lds = ALDS ? (unsigned)((m + 1) * ((k + kTileK - 1) / kTileK) * kTileK * 2) : 0u;
-  hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U>), dim3((unsigned)slabs), dim3(DW * 64), lds, st,
-                     ac, as, m, w, n, k, out, epi);
+  // grouped A fetch: whole 4-tile groups per row (k % 256 == 0) and 16-byte scale loads
+  const bool ga = !ALDS && U == 4 && k % 256 == 0 && (reinterpret_cast<uintptr_t>(as) & 15u) == 0;
+  if constexpr (!ALDS && U == 4) {
+    if (ga) {
+      hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, true>), dim3((unsigned)slabs),
+                         dim3(DW * 64), lds, st, ac, as, m, w, n, k, out, epi);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, false>), dim3((unsigned)slabs), dim3(DW * 64),
+                     lds, st, ac, as, m, w, n, k, out, epi);
 }
 
 template <int MFD, bool SILU>

@@ -75,6 +75,11 @@ def test_unit_scales_give_the_exact_integer_product(gpu_lib):
     (1, 33, 32, "f32"),          # smallest K
     (7, 1000, 5120, "bf16"),     # f16 decode kernel just above the FP4 path's rows, ragged N
     (5, 64, 320, "f32"),         # f16 decode kernel, a K of 1.25 weight super-tiles
+    # decode with A fetched in 4-tile groups (k % 256 == 0); wave ranges are whole
+    # groups, so some waves get none:
+    (20, 96, 768, "f32"),        # 3 groups over 4 waves
+    (45, 64, 256, "bf16"),       # 1 group over 2 waves, two row fragments
+    (32, 200, 1280, "bf16"),     # exactly one row fragment, ragged N
     (512, 256, 1024, "bf16"),
     # last-round cuts on 256 CUs (tiles of 256x256, two row blocks at M=512):
     (512, 33184, 256, "bf16"),   # 260 tiles: the last 4 run as 16 pieces of 64x64 each; ragged N
@@ -252,6 +257,7 @@ def test_fused_segments_small(gpu_lib, M):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 192, 256), (40, 192, 256), (130, 192, 256),
+                                   (20, 768, 256), (50, 512, 192),   # decode with grouped A fetch
                                    (512, 256, 38400),    # 300 gate/up tiles: the last 44 as 4 row bands each
                                    (512, 256, 43520)])   # 340 tiles: the last 84 as half-height tiles
 def test_silu_mul_small(gpu_lib, M, K, N):
