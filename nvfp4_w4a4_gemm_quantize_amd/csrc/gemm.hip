@@ -572,22 +572,39 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
 #endif
 
 // Which output tile a workgroup of the prefill kernel computes (1-D grids).
-// A full tile is `first + blockIdx.x / (ry * rx)` of a row-major grid gx full
-// tiles wide; the workgroup takes piece blockIdx.x % (ry * rx) of it, the
-// tile cut into ry row bands and rx column bands (ry = rx = 1: the whole
-// tile).  Pieces serve the last, partly filled round of a launch.
+// Tiles are numbered in groups of kGroupCols tile columns, row-major within a
+// group (the grid is gx tiles wide and gy tall).  A workgroup takes tile
+// `first + blockIdx.x / (ry * rx)` in that order, and piece
+// blockIdx.x % (ry * rx) of it: the tile cut into ry row bands and rx column
+// bands (ry = rx = 1: the whole tile; pieces serve the last, partly filled
+// round of a launch).
+// XCD-aware order (xcd_chunk > 0, whole tiles only): the hardware deals
+// workgroups to the kXcds XCDs in turn, so XCD x runs blocks x, x + kXcds,
+// ...; block b is given tile (b % kXcds) * xcd_chunk + b / kXcds, i.e. each
+// XCD works through a contiguous run of the order.  The 32 tiles an XCD holds
+// at once are then about 4 row bands x 8 columns: each weight slab is read by
+// 4 of them and each A band by 8 through the same L2, where the row-major
+// order spread a weight slab's tiles over several XCDs.
+constexpr int kXcds = 8;
+constexpr int kGroupCols = 8;
 struct TileMap {
-  int gx;
+  int gx, gy;
   int first;
-  int ry;
-  int rx;
+  int ry, rx;
+  int xcd_chunk;
 };
 
 __device__ __forceinline__ void map_tile(const TileMap& tm, int& bx, int& by) {
   const int per = tm.ry * tm.rx;
-  const int t = tm.first + (int)blockIdx.x / per, q = (int)blockIdx.x % per;
-  bx = (t % tm.gx) * tm.rx + q % tm.rx;
-  by = (t / tm.gx) * tm.ry + q / tm.rx;
+  int b = (int)blockIdx.x / per;
+  const int q = (int)blockIdx.x % per;
+  if (tm.xcd_chunk > 0) b = (b % kXcds) * tm.xcd_chunk + b / kXcds;
+  const int t = tm.first + b;
+  const int per_group = kGroupCols * tm.gy;
+  const int g = t / per_group, w = t - g * per_group;
+  const int width = min(kGroupCols, tm.gx - g * kGroupCols);
+  bx = (g * kGroupCols + w % width) * tm.rx + q % tm.rx;
+  by = (w / width) * tm.ry + q / tm.rx;
 }
 
 template <int MF, int NF, int WM, int WN, int NSTAGE>
@@ -1553,8 +1570,9 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
     }
     const bool cut = ry * rx > 1;
     const int64_t nbig = cut ? tiles - rem : tiles;
-    const TileMap big{(int)grid.x, 0, 1, 1};
-    const TileMap tail{(int)grid.x, (int)nbig, ry, rx};
+    const int xcd_chunk = nbig % kXcds == 0 ? (int)(nbig / kXcds) : 0;
+    const TileMap big{(int)grid.x, (int)grid.y, 0, 1, 1, xcd_chunk};
+    const TileMap tail{(int)grid.x, (int)grid.y, (int)nbig, ry, rx, 0};
     const dim3 tail_grid((unsigned)(rem * ry * rx));
 #define NVFP4_LAUNCH_PIECE(MFP, NFP, SL, GRID, MAP) \
   hipLaunchKernelGGL((gemm_prefill_dma_kernel<MFP, NFP, WM, WN, NS, SL, true>), GRID, block, 0, st, ac, as, m, w, n, \
