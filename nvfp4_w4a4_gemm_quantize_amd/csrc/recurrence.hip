@@ -24,8 +24,10 @@
 // growing gate, NaN) runs the unscaled update.
 //
 // Work split: the recurrence is sequential in time and independent per state
-// row, so a workgroup owns 16 rows of one head's state in registers for the
-// whole sequence (8 workgroups per head).  16 lanes share a row, each holding
+// row, so a workgroup owns 32 rows of one head's state in registers for the
+// whole sequence (4 workgroups per head, 8 waves each: with 48 heads one
+// workgroup per CU and two waves per SIMD, and each head's keys and queries
+// normalised by 4 workgroups rather than 8).  16 lanes share a row, each holding
 // 8 of its 128 columns (4j..4j+3 and 64+4j..64+4j+3 for lane j, so the 16
 // lanes' 16-byte LDS reads of a key are contiguous); the row's dot products
 // are summed across those lanes with DPP.  Inputs are staged 32 time steps at
@@ -47,12 +49,18 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kD = 128;          // key and value dimension of a head
-constexpr int kRows = 16;        // state rows per workgroup
-constexpr int kThreads = 256;    // 4 waves x 4 rows x 16 lanes
+constexpr int kRows = 32;        // state rows per workgroup
+constexpr int kThreads = 16 * kRows;   // 4 rows x 16 lanes per wave
 constexpr int kChunk = 32;       // time steps per LDS stage
 constexpr int kSeg = 8;          // time steps per segment of the scaled state
 static_assert(kChunk % kSeg == 0 && (kSeg & (kSeg - 1)) == 0, "segments tile a chunk");
-static_assert(kThreads == 16 * kRows && kChunk == 2 * (kThreads / 16), "a chunk's outputs are two steps per thread");
+// Staging maps: key/query pieces (8 bf16) are 16 per step, kThreads / 16
+// steps per pass; value rows move 8 bf16 per item; outputs are two per thread.
+constexpr int kStepsPerPass = kThreads / 16;
+constexpr int kKqPasses = kChunk / kStepsPerPass;
+constexpr int kVParts = kRows / 8;
+static_assert(kChunk % kStepsPerPass == 0 && kRows % 8 == 0 && kChunk * kVParts <= kThreads, "staging maps");
+static_assert(kChunk * kRows == 2 * kThreads, "a chunk's outputs are two per thread");
 constexpr float kNormEps = 1e-6f;
 
 struct Stage {
@@ -82,10 +90,11 @@ __device__ __forceinline__ float row_sum16(float x) {
 
 // Registers holding one chunk's raw inputs between its global loads and its
 // conversion into a Stage.  Thread t carries key and query pieces (8 bf16) of
-// steps t/16 and 16 + t/16, piece t%16; threads < 64 a value half-row (8
-// bf16) of step t/2; threads < kChunk the two gates of step t.
+// steps t/16 + p * kStepsPerPass, piece t%16; threads < kChunk * kVParts 8
+// bf16 of a value row (step t / kVParts, part t % kVParts); threads < kChunk
+// the two gates of step t.
 struct Raw {
-  uint4 k[2], q[2], v;
+  uint4 k[kKqPasses], q[kKqPasses], v;
   uint32_t beta, g;
 };
 
@@ -121,17 +130,17 @@ gdn_recurrence_kernel(GdnArgs a) {
   // first step times the leading dimension (a workgroup-uniform value).
   const int64_t koff = (int64_t)(t >> 4) * a.ld_k + hk * kD + 8 * (t & 15);
   const int64_t qoff = (int64_t)(t >> 4) * a.ld_q + hk * kD + 8 * (t & 15);
-  const int64_t voff = (int64_t)(t >> 1) * a.ld_v + (int64_t)h * kD + i0 + 8 * (t & 1);
+  const int64_t voff = (int64_t)(t / kVParts) * a.ld_v + (int64_t)h * kD + i0 + 8 * (t % kVParts);
   const int64_t boff = (int64_t)t * a.ld_beta + h, goff = (int64_t)t * a.ld_g + h;
   auto load = [&](int64_t chunk, Raw& R) __attribute__((always_inline)) {
     const int64_t t0 = chunk * kChunk;
     if (t0 + kChunk <= T) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        R.k[p] = *reinterpret_cast<const uint4*>(a.k + (t0 + 16 * p) * a.ld_k + koff);
-        R.q[p] = *reinterpret_cast<const uint4*>(a.q + (t0 + 16 * p) * a.ld_q + qoff);
+      for (int p = 0; p < kKqPasses; ++p) {
+        R.k[p] = *reinterpret_cast<const uint4*>(a.k + (t0 + kStepsPerPass * p) * a.ld_k + koff);
+        R.q[p] = *reinterpret_cast<const uint4*>(a.q + (t0 + kStepsPerPass * p) * a.ld_q + qoff);
       }
-      if (t < 2 * kChunk) R.v = *reinterpret_cast<const uint4*>(a.v + t0 * a.ld_v + voff);
+      if (t < kChunk * kVParts) R.v = *reinterpret_cast<const uint4*>(a.v + t0 * a.ld_v + voff);
       if (t < kChunk) {
         R.beta = a.beta[t0 * a.ld_beta + boff];
         R.g = a.g[t0 * a.ld_g + goff];
@@ -140,17 +149,17 @@ gdn_recurrence_kernel(GdnArgs a) {
     }
     // the last, partial chunk: steps past the end read the last step again
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      int64_t step = t0 + p * 16 + (t >> 4);
+    for (int p = 0; p < kKqPasses; ++p) {
+      int64_t step = t0 + p * kStepsPerPass + (t >> 4);
       step = step < T ? step : T - 1;
       const int col = hk * kD + 8 * (t & 15);
       R.k[p] = *reinterpret_cast<const uint4*>(a.k + step * a.ld_k + col);
       R.q[p] = *reinterpret_cast<const uint4*>(a.q + step * a.ld_q + col);
     }
-    if (t < 2 * kChunk) {
-      int64_t step = t0 + (t >> 1);
+    if (t < kChunk * kVParts) {
+      int64_t step = t0 + t / kVParts;
       step = step < T ? step : T - 1;
-      R.v = *reinterpret_cast<const uint4*>(a.v + step * a.ld_v + (int64_t)h * kD + i0 + 8 * (t & 1));
+      R.v = *reinterpret_cast<const uint4*>(a.v + step * a.ld_v + (int64_t)h * kD + i0 + 8 * (t % kVParts));
     }
     if (t < kChunk) {
       int64_t step = t0 + t;
@@ -169,8 +178,8 @@ gdn_recurrence_kernel(GdnArgs a) {
   };
   auto store = [&](const Raw& R, Stage& S) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int step = p * 16 + (t >> 4), pc = t & 15;
+    for (int p = 0; p < kKqPasses; ++p) {
+      const int step = p * kStepsPerPass + (t >> 4), pc = t & 15;
       float kf[8], qf[8];
       unpack8(R.k[p], kf);
       unpack8(R.q[p], qf);
@@ -194,10 +203,10 @@ gdn_recurrence_kernel(GdnArgs a) {
       qd[1] = make_float4(qf[4] * nq, qf[5] * nq, qf[6] * nq, qf[7] * nq);
       if (pc == 0) S.sc[step].z = kq * nk * nq;
     }
-    if (t < 2 * kChunk) {
+    if (t < kChunk * kVParts) {
       float vf[8];
       unpack8(R.v, vf);
-      float4* vd = reinterpret_cast<float4*>(&S.v[t >> 1][8 * (t & 1)]);
+      float4* vd = reinterpret_cast<float4*>(&S.v[t / kVParts][8 * (t % kVParts)]);
       vd[0] = make_float4(vf[0], vf[1], vf[2], vf[3]);
       vd[1] = make_float4(vf[4], vf[5], vf[6], vf[7]);
     }
@@ -219,7 +228,7 @@ gdn_recurrence_kernel(GdnArgs a) {
     }
   };
 
-  const int64_t ooff = (int64_t)(t >> 4) * a.ld_o + (int64_t)h * kD + i0 + (t & 15);
+  const int64_t ooff = (int64_t)(t / kRows) * a.ld_o + (int64_t)h * kD + i0 + (t % kRows);
   Raw R;
   load(0, R);
   store(R, st[0]);
@@ -296,13 +305,13 @@ gdn_recurrence_kernel(GdnArgs a) {
     }
     __syncthreads();
     if (c + 1 < nchunks) store(R, st[(c + 1) & 1]);
-    // this chunk's outputs: kChunk x 16 values, two per thread (steps
-    // t/16 and 16 + t/16, row t%16)
+    // this chunk's outputs: kChunk x kRows values, two per thread (steps
+    // t/kRows and kChunk/2 + t/kRows, row t%kRows)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int step = (t >> 4) + 16 * e, r = t & 15;
+      const int step = t / kRows + (kChunk / 2) * e, r = t % kRows;
       if (step < cnt) {
-        const int64_t off = (c * kChunk + 16 * e) * a.ld_o + ooff;
+        const int64_t off = (c * kChunk + (kChunk / 2) * e) * a.ld_o + ooff;
         const float val = obuf[step][r];
         if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[off] = f32_to_bf16_rne(val);
         else reinterpret_cast<float*>(a.o)[off] = val;
