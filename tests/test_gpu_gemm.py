@@ -302,3 +302,44 @@ def test_empty_m_is_a_no_op(gpu_lib):
     asc = torch.empty((0, 8), dtype=torch.uint8, device="cuda")
     y = gpu_lib.gemm_w4a4(ac, asc, f32([1.0]), packed, wg, 64, 128, out_dtype=torch.float32)
     assert y.shape == (0, 64)
+
+
+# Every output element of the full-size launches is written, exactly once in
+# effect: the output starts as NaN, must come back finite, and a second run
+# must reproduce it bit for bit.  This covers the launch splitting (full rounds
+# plus cut tail pieces) and the XCD-aware tile order at the bench's shapes,
+# where the oracle comparisons above sample rows.
+FULL_SHAPES = {
+    "gdn_inproj": (4096, 16480, 5120, "gdn"),
+    "gate_up": (4096, 34816, 5120, "silu_mul"),
+    "down": (4096, 5120, 17408, "none"),
+    "linear": (2048, 5120, 5120, "none"),
+    "decode_m64": (64, 17408, 5120, "none"),
+    "decode_m8_gate_up": (8, 34816, 5120, "silu_mul"),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SHAPES))
+def test_full_size_every_output_written(gpu_lib, name):
+    M, N, K, epi = FULL_SHAPES[name]
+    gen = torch.Generator(device="cuda").manual_seed(1000 + list(FULL_SHAPES).index(name))
+    a = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    ac, asc, ag = gpu_lib.nvfp4_quantize(a)
+    offs = [0, 2048, 4096, 10240, 16384, 16432, 16480] if epi == "gdn" else None
+    packed, wg = gpu_lib.nvfp4_pack_weights(w, offs)
+    del w
+    n_out = N // 2 if epi == "silu_mul" else N
+    outs = []
+    for _ in range(2):
+        y = torch.full((M, n_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if epi == "gdn":
+            zeros = torch.zeros(48, dtype=torch.float32, device="cuda")
+            gpu_lib.gemm_w4a4_fused_segments(ac, asc, ag, packed, N, K, offs, wg,
+                                             ["none"] * 4 + ["sigmoid", "gdn_decay"], zeros, zeros, out=y)
+        else:
+            gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out=y, epilogue=epi)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0].float()).all()), "%s: output elements left unwritten" % name
+    assert torch.equal(outs[0], outs[1]), "%s: runs differ" % name
