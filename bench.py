@@ -26,7 +26,8 @@ reported as weight GB/s (packed weight bytes / GEMM time).  Kernel durations
 for the roofline are taken with HIP events on the stream the kernels run on,
 in every other timed step; the part totals behind `value` come from the
 steps in between, which record no events between kernels (each such event
-delays the next kernel by about 6 us).  Weight packing is offline (done
+delays the next kernel by about 6 us).  Durations are medians over their
+steps (50 timed steps after 10 warm-up steps by default).  Weight packing is offline (done
 once, outside the timed region).
 """
 import argparse
@@ -50,7 +51,7 @@ DECODE_COPIES = 8
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=40)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
@@ -499,10 +500,10 @@ def main():
     progress("%d timed steps done" % args.steps)
     ins = [e for e, f in zip(evs, inner) if f]
     tot = [e for e, f in zip(evs, inner) if not f] or ins
-    mean_ms = lambda es, n: sum(e[n][0].elapsed_time(e[n][1]) for e in es) / len(es)
-    dur = {n: mean_ms(tot, n) for n in OUTER_EVENTS}
-    dur.update({n: mean_ms(ins, n) for n in INNER_EVENTS})
-    prefill_instrumented_ms = mean_ms(ins, "prefill")
+    median_ms = lambda es, n: float(np.median([e[n][0].elapsed_time(e[n][1]) for e in es]))
+    dur = {n: median_ms(tot, n) for n in OUTER_EVENTS}
+    dur.update({n: median_ms(ins, n) for n in INNER_EVENTS})
+    prefill_instrumented_ms = median_ms(ins, "prefill")
     prefill_flop = FLOP["gdn"] + FLOP["gate_up"] + FLOP["down"]
     value = prefill_flop / (dur["prefill"] * 1e-3) / 1e12
     gemm_ms = dur["gdn"] + dur["gate_up"] + dur["down"]
