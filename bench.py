@@ -471,8 +471,8 @@ def gdn_recurrence_run(torch, B, S, reps=5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one MI355X: the library has no multi-GPU path and this build uses one GPU "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one MI355X: the library has no multi-GPU path (the projections would shard "
+              "by output columns, the down-projection by K); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     from nvfp4_w4a4_gemm_quantize_amd import binding as B

@@ -64,7 +64,7 @@ typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
 #define NVFP4_EINVAL (-1)       /* null pointer, unknown enum value, bad count */
 #define NVFP4_ESHAPE (-2)       /* sizes that violate a stated shape rule */
 #define NVFP4_EALIGN (-3)       /* pointer or leading dimension not aligned */
-#define NVFP4_EUNSUPPORTED (-4) /* valid request outside what this build runs */
+#define NVFP4_EUNSUPPORTED (-4) /* valid request outside what this library implements */
 #define NVFP4_EHIP (-5)         /* a HIP launch failed (see nvfp4_last_hip_error) */
 #define NVFP4_ESIZE (-6)        /* a caller buffer is smaller than required */
 

@@ -170,7 +170,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_EINVAL: return "invalid argument (null pointer, unknown enum value or count)";
     case NVFP4_ESHAPE: return "shape rule violated";
     case NVFP4_EALIGN: return "pointer or leading dimension misaligned";
-    case NVFP4_EUNSUPPORTED: return "valid request not supported by this build";
+    case NVFP4_EUNSUPPORTED: return "valid request not supported by this library";
     case NVFP4_EHIP: return "HIP launch failed";
     case NVFP4_ESIZE: return "caller buffer too small";
     default: return "unknown status";

@@ -111,7 +111,7 @@ def gm(lib, ac=A16, asc=A16, ag=A16, m=64, w=A16, wg=A16, n=128, k=128, out=A16,
 
 
 def test_gemm_validation(lib):
-    assert gm(lib, k=48) == EUNSUPPORTED       # a valid NVFP4 K (16 | K) this build does not run
+    assert gm(lib, k=48) == EUNSUPPORTED       # a valid NVFP4 K (16 | K) the library does not run
     assert gm(lib, k=40) == ESHAPE
     assert gm(lib, n=0) == ESHAPE
     assert gm(lib, m=-3) == ESHAPE
