@@ -256,14 +256,15 @@ gdn_recurrence_kernel(GdnArgs a) {
       constexpr bool kScaled = decltype(scaled_tag)::value;
       const float4 ka = x.ka, kb = x.kb, qa = x.qa, qb = x.qb, sc = x.sc;
       const float vi = x.vi;
-      float sk0 = s[0] * ka.x, sk1 = s[1] * ka.y, sq0 = s[0] * qa.x, sq1 = s[1] * qa.y;
-      sk0 = fmaf(s[2], ka.z, sk0); sk1 = fmaf(s[3], ka.w, sk1);
-      sq0 = fmaf(s[2], qa.z, sq0); sq1 = fmaf(s[3], qa.w, sq1);
-      sk0 = fmaf(s[4], kb.x, sk0); sk1 = fmaf(s[5], kb.y, sk1);
-      sq0 = fmaf(s[4], qb.x, sq0); sq1 = fmaf(s[5], qb.y, sq1);
-      sk0 = fmaf(s[6], kb.z, sk0); sk1 = fmaf(s[7], kb.w, sk1);
-      sq0 = fmaf(s[6], qb.z, sq0); sq1 = fmaf(s[7], qb.w, sq1);
-      const float sk = row_sum16(sk0 + sk1), sq = row_sum16(sq0 + sq1);
+      float sk0 = s[0] * ka.x, sq0 = s[0] * qa.x;
+      sk0 = fmaf(s[1], ka.y, sk0); sq0 = fmaf(s[1], qa.y, sq0);
+      sk0 = fmaf(s[2], ka.z, sk0); sq0 = fmaf(s[2], qa.z, sq0);
+      sk0 = fmaf(s[3], ka.w, sk0); sq0 = fmaf(s[3], qa.w, sq0);
+      sk0 = fmaf(s[4], kb.x, sk0); sq0 = fmaf(s[4], qb.x, sq0);
+      sk0 = fmaf(s[5], kb.y, sk0); sq0 = fmaf(s[5], qb.y, sq0);
+      sk0 = fmaf(s[6], kb.z, sk0); sq0 = fmaf(s[6], qb.z, sq0);
+      sk0 = fmaf(s[7], kb.w, sk0); sq0 = fmaf(s[7], qb.w, sq0);
+      const float sk = row_sum16(sk0), sq = row_sum16(sq0);
       const float kv[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
       const float beta = sc.y;
       if constexpr (kScaled) {
