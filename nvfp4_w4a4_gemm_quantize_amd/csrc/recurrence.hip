@@ -30,8 +30,10 @@
 // normalised by 4 workgroups rather than 8).  16 lanes share a row, each holding
 // 8 of its 128 columns (4j..4j+3 and 64+4j..64+4j+3 for lane j, so the 16
 // lanes' 16-byte LDS reads of a key are contiguous); the row's dot products
-// are summed across those lanes with DPP.  Inputs are staged 32 time steps at
-// a time through double-buffered LDS: while a chunk is being consumed the
+// are summed across those lanes with DPP.  Inputs are staged 64 time steps at
+// a time (155 KB of LDS for both buffers; a workgroup of 8 waves at this
+// register count holds a CU alone anyway) through double-buffered LDS, which
+// halves the chunk-boundary barriers of 32-step chunks: while a chunk is being consumed the
 // next one is loaded into registers, then converted -- keys and queries to
 // normalised fp32 (their norms reduced once per step per workgroup), gates to
 // (alpha, beta, k^.q^, A, 1/A) -- and written to the other buffer; within a
@@ -51,8 +53,9 @@ namespace {
 constexpr int kD = 128;          // key and value dimension of a head
 constexpr int kRows = 32;        // state rows per workgroup
 constexpr int kThreads = 16 * kRows;   // 4 rows x 16 lanes per wave
-constexpr int kChunk = 32;       // time steps per LDS stage
+constexpr int kChunk = 64;       // time steps per LDS stage
 constexpr int kSeg = 8;          // time steps per segment of the scaled state
+constexpr float kRangeLo = 0x1p-12f, kRangeHi = 0x1p12f;   // decays that keep A within [2^-96, 2^96]
 static_assert(kChunk % kSeg == 0 && (kSeg & (kSeg - 1)) == 0, "segments tile a chunk");
 // Staging maps: key/query pieces (8 bf16) are 16 per step, kThreads / 16
 // steps per pass; value rows move 8 bf16 per item; outputs are two per thread.
@@ -60,7 +63,8 @@ constexpr int kStepsPerPass = kThreads / 16;
 constexpr int kKqPasses = kChunk / kStepsPerPass;
 constexpr int kVParts = kRows / 8;
 static_assert(kChunk % kStepsPerPass == 0 && kRows % 8 == 0 && kChunk * kVParts <= kThreads, "staging maps");
-static_assert(kChunk * kRows == 2 * kThreads, "a chunk's outputs are two per thread");
+constexpr int kOutPerThread = kChunk * kRows / kThreads, kOutStepStride = kThreads / kRows;
+static_assert(kChunk * kRows % kThreads == 0, "outputs per thread");
 constexpr float kNormEps = 1e-6f;
 
 struct Stage {
@@ -222,7 +226,7 @@ gdn_recurrence_kernel(GdnArgs a) {
         if ((t & (kSeg - 1)) >= off) A *= y;
       }
       S.sa[t] = make_float2(A, __builtin_amdgcn_rcpf(A));      // within 1 ulp
-      const bool in_range = alpha >= 0x1p-12f && alpha <= 0x1p12f;    // false for NaN
+      const bool in_range = alpha >= kRangeLo && alpha <= kRangeHi;    // false for NaN
       const uint64_t out = __ballot(!in_range);
       if (t == 0) S.scaled = out == 0;
     }
@@ -309,10 +313,10 @@ gdn_recurrence_kernel(GdnArgs a) {
     // this chunk's outputs: kChunk x kRows values, two per thread (steps
     // t/kRows and kChunk/2 + t/kRows, row t%kRows)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int step = t / kRows + (kChunk / 2) * e, r = t % kRows;
+    for (int e = 0; e < kOutPerThread; ++e) {
+      const int step = t / kRows + kOutStepStride * e, r = t % kRows;
       if (step < cnt) {
-        const int64_t off = (c * kChunk + (kChunk / 2) * e) * a.ld_o + ooff;
+        const int64_t off = (c * kChunk + kOutStepStride * e) * a.ld_o + ooff;
         const float val = obuf[step][r];
         if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[off] = f32_to_bf16_rne(val);
         else reinterpret_cast<float*>(a.o)[off] = val;

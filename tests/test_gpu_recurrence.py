@@ -61,8 +61,10 @@ def _with_resets(d, seed):
 @pytest.mark.parametrize("T,hk,hv,with_init,bf16_out,resets", [
     (300, 2, 6, True, False, False),     # ragged last chunk, grouped key heads, initial state
     (1, 1, 1, False, False, False),      # a single step
-    (32, 1, 2, True, True, False),       # exactly one chunk; bf16 output
-    (33, 4, 4, False, False, False),     # one step into the second chunk
+    (32, 1, 2, True, True, False),       # half a 64-step chunk (the partial-chunk loop only); bf16 output
+    (33, 4, 4, False, False, False),
+    (64, 1, 3, True, True, False),       # exactly one chunk
+    (65, 2, 2, False, False, False),     # one step into the second chunk
     (640, 2, 6, True, False, True),      # decays outside [2^-12, 2^12] in some chunks
     (301, 1, 3, False, True, True),
 ])
