@@ -16,7 +16,9 @@
 //     u = A (S^ . k^),  c = beta (v - u),  o = A (S^ . q^) + c (k^ . q^),
 //     S^ <- S^ + (c / A) k^,
 // one multiply-add per element instead of a multiply and a multiply-add; at
-// the segment's end S = A S^ is restored.  Floating point being scale-free,
+// the segment's end S = A S^ is restored.  The stage holds beta v (exact: both
+// are bf16) and beta A, so the write coefficient c = beta v - (beta A)(S^.k^)
+// is a single multiply-add (likewise beta alpha for the unscaled update).  Floating point being scale-free,
 // this changes only which products are rounded: the state's effective decay
 // per step is the ratio of two consecutive rounded A, within a few units of
 // roundoff of alpha.  A chunk whose decays all lie in [2^-12, 2^12] keeps A
@@ -70,9 +72,9 @@ constexpr float kNormEps = 1e-6f;
 struct Stage {
   float kn[kChunk][kD];     // normalised keys
   float qn[kChunk][kD];     // normalised queries
-  float v[kChunk][kRows];   // this workgroup's value rows
-  float4 sc[kChunk];        // alpha, beta, k^ . q^, unused
-  float2 sa[kChunk];        // A (decay product since the step's 8-step segment began), 1 / A
+  float v[kChunk][kRows];   // beta times this workgroup's value rows (exact: both are bf16)
+  float4 gs[kChunk];        // scaled update: A (decay product since the step's 8-step segment began), 1 / A, beta A, k^ . q^
+  float4 gu[kChunk];        // plain update: alpha, beta alpha, k^ . q^, unused
   int scaled;               // every decay of the chunk within [2^-12, 2^12]
 };
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ float row_sum16(float x) {
 // the two gates of step t.
 struct Raw {
   uint4 k[kKqPasses], q[kKqPasses], v;
-  uint32_t beta, g;
+  uint32_t beta, g, vbeta;   // vbeta: the write strength of the value item's step
 };
 
 }  // namespace
@@ -136,6 +138,7 @@ gdn_recurrence_kernel(GdnArgs a) {
   const int64_t qoff = (int64_t)(t >> 4) * a.ld_q + hk * kD + 8 * (t & 15);
   const int64_t voff = (int64_t)(t / kVParts) * a.ld_v + (int64_t)h * kD + i0 + 8 * (t % kVParts);
   const int64_t boff = (int64_t)t * a.ld_beta + h, goff = (int64_t)t * a.ld_g + h;
+  const int64_t vboff = (int64_t)(t / kVParts) * a.ld_beta + h;
   auto load = [&](int64_t chunk, Raw& R) __attribute__((always_inline)) {
     const int64_t t0 = chunk * kChunk;
     if (t0 + kChunk <= T) {
@@ -144,7 +147,10 @@ gdn_recurrence_kernel(GdnArgs a) {
         R.k[p] = *reinterpret_cast<const uint4*>(a.k + (t0 + kStepsPerPass * p) * a.ld_k + koff);
         R.q[p] = *reinterpret_cast<const uint4*>(a.q + (t0 + kStepsPerPass * p) * a.ld_q + qoff);
       }
-      if (t < kChunk * kVParts) R.v = *reinterpret_cast<const uint4*>(a.v + t0 * a.ld_v + voff);
+      if (t < kChunk * kVParts) {
+        R.v = *reinterpret_cast<const uint4*>(a.v + t0 * a.ld_v + voff);
+        R.vbeta = a.beta[t0 * a.ld_beta + vboff];
+      }
       if (t < kChunk) {
         R.beta = a.beta[t0 * a.ld_beta + boff];
         R.g = a.g[t0 * a.ld_g + goff];
@@ -164,6 +170,7 @@ gdn_recurrence_kernel(GdnArgs a) {
       int64_t step = t0 + t / kVParts;
       step = step < T ? step : T - 1;
       R.v = *reinterpret_cast<const uint4*>(a.v + step * a.ld_v + (int64_t)h * kD + i0 + 8 * (t % kVParts));
+      R.vbeta = a.beta[step * a.ld_beta + h];
     }
     if (t < kChunk) {
       int64_t step = t0 + t;
@@ -205,19 +212,25 @@ gdn_recurrence_kernel(GdnArgs a) {
       kd[1] = make_float4(kf[4] * nk, kf[5] * nk, kf[6] * nk, kf[7] * nk);
       qd[0] = make_float4(qf[0] * nq, qf[1] * nq, qf[2] * nq, qf[3] * nq);
       qd[1] = make_float4(qf[4] * nq, qf[5] * nq, qf[6] * nq, qf[7] * nq);
-      if (pc == 0) S.sc[step].z = kq * nk * nq;
+      if (pc == 0) {
+        const float kqn = kq * nk * nq;
+        S.gs[step].w = kqn;
+        S.gu[step].z = kqn;
+      }
     }
     if (t < kChunk * kVParts) {
       float vf[8];
       unpack8(R.v, vf);
+      const float bv = bf16f(R.vbeta & 0xFFFFu);
       float4* vd = reinterpret_cast<float4*>(&S.v[t / kVParts][8 * (t % kVParts)]);
-      vd[0] = make_float4(vf[0], vf[1], vf[2], vf[3]);
-      vd[1] = make_float4(vf[4], vf[5], vf[6], vf[7]);
+      vd[0] = make_float4(vf[0] * bv, vf[1] * bv, vf[2] * bv, vf[3] * bv);
+      vd[1] = make_float4(vf[4] * bv, vf[5] * bv, vf[6] * bv, vf[7] * bv);
     }
     if (t < kChunk) {
       const float alpha = expf(bf16f(R.g & 0xFFFFu));
-      S.sc[t].x = alpha;
-      S.sc[t].y = bf16f(R.beta & 0xFFFFu);
+      const float beta = bf16f(R.beta & 0xFFFFu);
+      S.gu[t].x = alpha;
+      S.gu[t].y = beta * alpha;
       // product of the decays from the segment's first step to this one
       float A = alpha;
 #pragma unroll
@@ -225,7 +238,9 @@ gdn_recurrence_kernel(GdnArgs a) {
         const float y = __shfl_up(A, off, kSeg);
         if ((t & (kSeg - 1)) >= off) A *= y;
       }
-      S.sa[t] = make_float2(A, __builtin_amdgcn_rcpf(A));      // within 1 ulp
+      S.gs[t].x = A;
+      S.gs[t].y = __builtin_amdgcn_rcpf(A);      // within 1 ulp
+      S.gs[t].z = beta * A;
       const bool in_range = alpha >= kRangeLo && alpha <= kRangeHi;    // false for NaN
       const uint64_t out = __ballot(!in_range);
       if (t == 0) S.scaled = out == 0;
@@ -244,22 +259,21 @@ gdn_recurrence_kernel(GdnArgs a) {
     // One time step for this lane's eight state elements, scaled (S^ = S / A)
     // or not.  Every lane of a row holds the row's output (identical bits), so
     // all of them write it.
-    struct In { float4 ka, kb, qa, qb, sc; float2 sa; float vi; };
-    auto fetch = [&](int step) __attribute__((always_inline)) {
+    struct In { float4 ka, kb, qa, qb, g; float vi; };
+    auto fetch = [&](int step, auto scaled_tag) __attribute__((always_inline)) {
       In x;
       x.ka = reinterpret_cast<const float4*>(S.kn[step])[lr];
       x.kb = reinterpret_cast<const float4*>(S.kn[step])[16 + lr];
       x.qa = reinterpret_cast<const float4*>(S.qn[step])[lr];
       x.qb = reinterpret_cast<const float4*>(S.qn[step])[16 + lr];
-      x.sc = S.sc[step];
-      x.sa = S.sa[step];
+      x.g = decltype(scaled_tag)::value ? S.gs[step] : S.gu[step];
       x.vi = S.v[step][rloc];
       return x;
     };
     auto compute = [&](int step, const In& x, auto scaled_tag) __attribute__((always_inline)) {
       constexpr bool kScaled = decltype(scaled_tag)::value;
-      const float4 ka = x.ka, kb = x.kb, qa = x.qa, qb = x.qb, sc = x.sc;
-      const float vi = x.vi;
+      const float4 ka = x.ka, kb = x.kb, qa = x.qa, qb = x.qb, g = x.g;
+      const float bvi = x.vi;           // beta v
       float sk0 = s[0] * ka.x, sq0 = s[0] * qa.x;
       sk0 = fmaf(s[1], ka.y, sk0); sq0 = fmaf(s[1], qa.y, sq0);
       sk0 = fmaf(s[2], ka.z, sk0); sq0 = fmaf(s[2], qa.z, sq0);
@@ -270,32 +284,32 @@ gdn_recurrence_kernel(GdnArgs a) {
       sk0 = fmaf(s[7], kb.w, sk0); sq0 = fmaf(s[7], qb.w, sq0);
       const float sk = row_sum16(sk0), sq = row_sum16(sq0);
       const float kv[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
-      const float beta = sc.y;
       if constexpr (kScaled) {
-        const float2 sa = x.sa;
-        const float cw = beta * (vi - sa.x * sk);
-        obuf[step][rloc] = fmaf(sa.x, sq, cw * sc.z);
-        const float d = cw * sa.y;
+        // g = (A, 1/A, beta A, k^.q^): c = beta v - beta A (S^.k^)
+        const float cw = fmaf(-g.z, sk, bvi);
+        obuf[step][rloc] = fmaf(g.x, sq, cw * g.w);
+        const float d = cw * g.y;
 #pragma unroll
         for (int j = 0; j < 8; ++j) s[j] = fmaf(d, kv[j], s[j]);
         if ((step & (kSeg - 1)) == kSeg - 1) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) s[j] *= sa.x;
+          for (int j = 0; j < 8; ++j) s[j] *= g.x;
         }
       } else {
-        const float alpha = sc.x;
-        const float cw = beta * (vi - alpha * sk);
-        obuf[step][rloc] = fmaf(alpha, sq, cw * sc.z);
+        // g = (alpha, beta alpha, k^.q^, -): c = beta v - beta alpha (S.k^)
+        const float alpha = g.x;
+        const float cw = fmaf(-g.y, sk, bvi);
+        obuf[step][rloc] = fmaf(alpha, sq, cw * g.z);
 #pragma unroll
         for (int j = 0; j < 8; ++j) s[j] = fmaf(alpha, s[j], cw * kv[j]);
       }
     };
     auto run_full = [&](auto scaled_tag) __attribute__((always_inline)) {
-      In cur = fetch(0);
+      In cur = fetch(0, scaled_tag);
 #pragma unroll
       for (int step = 0; step < kChunk; ++step) {
         In nxt;
-        if (step + 1 < kChunk) nxt = fetch(step + 1);
+        if (step + 1 < kChunk) nxt = fetch(step + 1, scaled_tag);
         asm volatile("" ::: "memory");
         compute(step, cur, scaled_tag);
         cur = nxt;
@@ -306,7 +320,7 @@ gdn_recurrence_kernel(GdnArgs a) {
     } else if (cnt == kChunk) {
       run_full(std::false_type{});
     } else {
-      for (int step = 0; step < cnt; ++step) compute(step, fetch(step), std::false_type{});
+      for (int step = 0; step < cnt; ++step) compute(step, fetch(step, std::false_type{}), std::false_type{});
     }
     __syncthreads();
     if (c + 1 < nchunks) store(R, st[(c + 1) & 1]);
