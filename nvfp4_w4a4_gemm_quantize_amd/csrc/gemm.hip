@@ -632,21 +632,23 @@ struct DmaShape {
 };
 
 // Global -> LDS DMA of 16 (or 4) bytes per lane: lane l's bytes land at
-// dst + l*16 (l*4).  Written as a single instruction in inline asm so the
-// compiler does not add its own (conservative, pipeline-draining) vmcnt waits
-// before later LDS reads; completion is tracked explicitly with wait_vmcnt
-// and published to the other waves with the barrier.  The instruction has no
-// register results (its data goes to LDS); the address registers are read at
-// issue.  M0 holds the wave-uniform LDS destination; the leading s_nop covers
-// the M0-write -> LDS-DMA hazard.
+// dst + l*16 (l*4), read from sbase + voff (a wave-uniform base in SGPRs and a
+// 32-bit per-lane offset, so the per-stage address steps are scalar adds).
+// Written as a single instruction in inline asm so the compiler does not add
+// its own (conservative, pipeline-draining) vmcnt waits before later LDS
+// reads; completion is tracked explicitly with wait_vmcnt and published to
+// the other waves with the barrier.  The instruction has no register results
+// (its data goes to LDS); the address registers are read at issue.  M0 holds
+// the wave-uniform LDS destination; the leading s_nop covers the M0-write ->
+// LDS-DMA hazard.
 __device__ __forceinline__ uint32_t lds_offset(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
-__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_offset(dst)) : "memory");
+__device__ __forceinline__ void dma16s(const uint8_t* sbase, uint32_t voff, uint8_t* dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_offset(dst)) : "memory");
 }
-__device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_offset(dst)) : "memory");
+__device__ __forceinline__ void dma4s(const uint8_t* sbase, uint32_t voff, uint8_t* dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_offset(dst)) : "memory");
 }
 // Compiler-only fence: no memory access is moved across it.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -714,26 +716,35 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   // W scale pairs; class sizes are multiples of the wave count, so load i of
   // every wave belongs to the same class (known at compile time).
   constexpr int I_AS = P::PC_AC, I_BC = I_AS + P::PC_AS, I_BS = I_BC + P::PC_BC;
+  // Wave-uniform bases (SGPRs, advanced per stage) and per-lane offsets.
   const uint8_t* src[P::LPW];
+  uint32_t voff[P::LPW];
   int dst[P::LPW];
 #pragma unroll
   for (int i = 0; i < P::LPW; ++i) {
     if (i < I_AS) {
       const int f = (wave + i * NWAVES) % P::N_AC;
-      src[i] = a_codes + row_of(m0 + 32 * f + r) * a_row_bytes + h * 16;
+      src[i] = a_codes;
+      voff[i] = (uint32_t)(row_of(m0 + 32 * f + r) * a_row_bytes) + h * 16;
       dst[i] = f * 1024;
     } else if (i < I_BC) {
       const int g = (wave + (i - I_AS) * NWAVES) % P::N_AS;
-      src[i] = a_scales + row_of(m0 + 64 * g + lane) * a_row_scales;
+      src[i] = a_scales;
+      voff[i] = (uint32_t)(row_of(m0 + 64 * g + lane) * a_row_scales);
       dst[i] = P::OFF_AS + g * 256;
     } else if (i < I_BS) {
       const int tl = (wave + (i - I_BC) * NWAVES) % P::N_BC;
-      src[i] = w_packed + tile_code_off(ntile_of(tl), 0, KS) + lane * 16;
+      src[i] = w_packed + tile_code_off(ntile_of(tl), 0, KS);
+      voff[i] = lane * 16;
       dst[i] = P::OFF_BC + tl * 1024;
     } else {
       const int p = (wave + (i - I_BS) * NWAVES) % P::N_BS;
-      const int tl = 2 * p + h;
-      src[i] = w_packed + tile_scale_off(ntile_of(tl), 0, KS, r);
+      // the pair's two tiles (h = 0, 1) differ per lane half: the tile's base
+      // offset goes in the lane part
+      const int64_t o0 = tile_scale_off(ntile_of(2 * p), 0, KS, 0);
+      const int64_t o1 = tile_scale_off(ntile_of(2 * p + 1), 0, KS, 0);
+      src[i] = w_packed + o0;
+      voff[i] = (uint32_t)(h ? o1 - o0 : 0) + r * 8;
       dst[i] = P::OFF_BS + p * 256;
     }
   }
@@ -748,10 +759,10 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     constexpr int W_SCALE_STEP = T == 0 ? 4 : T == 1 ? kTileN * 8 - 4 : T == 2 ? 4 : kSuperBytes - kTileN * 8 - 4;
 #pragma unroll
     for (int i = 0; i < P::LPW; ++i) {
-      if (i < I_AS) { dma16(src[i], base + dst[i]); src[i] += 32; }
-      else if (i < I_BC) { dma4(src[i], base + dst[i]); src[i] += 4; }
-      else if (i < I_BS) { dma16(src[i], base + dst[i]); src[i] += W_CODE_STEP; }
-      else { dma4(src[i], base + dst[i]); src[i] += W_SCALE_STEP; }
+      if (i < I_AS) { dma16s(src[i], voff[i], base + dst[i]); src[i] += 32; }
+      else if (i < I_BC) { dma4s(src[i], voff[i], base + dst[i]); src[i] += 4; }
+      else if (i < I_BS) { dma16s(src[i], voff[i], base + dst[i]); src[i] += W_CODE_STEP; }
+      else { dma4s(src[i], voff[i], base + dst[i]); src[i] += W_SCALE_STEP; }
     }
   };
 
@@ -1547,7 +1558,11 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
   const int64_t bn = epi.silu_mul ? BN / 2 : BN;
   dim3 grid((unsigned)((cols + bn - 1) / bn), (unsigned)((m + BM - 1) / BM));
   dim3 block(WM * WN * 64);
-  if ((k & 63) == 0 && k / kTileK >= NS) {
+  // The DMA kernel addresses A through 32-bit per-lane offsets from a
+  // wave-uniform base: A's codes must stay below 4 GiB (else the register-staged
+  // kernel, with full 64-bit addresses, runs).
+  const bool a_fits_32 = m * (k / 2) < ((int64_t)1 << 32) - 64;
+  if ((k & 63) == 0 && k / kTileK >= NS && a_fits_32) {
     // One workgroup per CU at a time: when the last round would leave most
     // CUs idle, its tiles run as a second launch of smaller pieces -- each
     // tile cut into ry row bands and rx column bands, the finest cut whose
