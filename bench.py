@@ -279,11 +279,17 @@ ALGO_BYTES = {
 
 
 def kernel_source_sha256():
+    """SHA-256 of the GEMM kernel sources with comments and runs of white space
+    removed: an edit to comments alone leaves the kernels, and the hash, as they were."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
     return h.hexdigest()
 
 

@@ -711,7 +711,8 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   };
   auto row_of = [&](int64_t row) -> int64_t { return row < m ? row : m - 1; };
 
-  // Per-lane source addresses (K step 0) and LDS offsets of this wave's loads.
+  // Source addresses (K step 0: a wave-uniform base plus a per-lane offset)
+  // and LDS offsets of this wave's loads.
   // Load classes in order: A code fragments, A scale groups (64 rows), W tiles,
   // W scale pairs; class sizes are multiples of the wave count, so load i of
   // every wave belongs to the same class (known at compile time).
@@ -748,8 +749,9 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
       dst[i] = P::OFF_BS + p * 256;
     }
   }
-  // Stages are issued strictly in order, so each load keeps a running source
-  // pointer that advances by its per-stage stride after every issue.  With
+  // Stages are issued strictly in order, so each load keeps a running
+  // (wave-uniform) base that advances by its per-stage stride after every
+  // issue; the per-lane offsets stay fixed.  With
   // four stages, the buffer of a stage is its tile's position T in the weight
   // super-tile, which fixes the weight strides at compile time.
   static_assert(NSTAGE == kSuperTiles, "one stage buffer per tile of a weight super-tile");
