@@ -808,11 +808,18 @@ if constexpr (PIPE) {
     }
   };
   const uint32_t hsh = 16u * h;   // bit offset of this lane's scale pair
+  // Serpentine order: consecutive MFMAs always share one operand, also across
+  // rows.  The chip runs this kernel power-limited, and fewer changing operand
+  // bits let it clock a little higher.  Each accumulator still sees its
+  // products in K order, so the results do not change.
   auto mma = [&](const half8_t (&av)[MF], const half8_t (&bv)[NF]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
-      for (int j = 0; j < NF; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+      for (int jj = 0; jj < NF; ++jj) {
+        const int j = (i & 1) ? NF - 1 - jj : jj;
+        acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+      }
   };
   // One MFMA, then a few VALU ops, for every MFMA of a sub-step.
   auto interleave = [&]() __attribute__((always_inline)) {
