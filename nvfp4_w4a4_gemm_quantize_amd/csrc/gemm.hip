@@ -280,43 +280,6 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
   }
 }
 
-// One 64-wide K step of a wave: MF x NF fragments, 4 sub-steps of 16 K each.
-// ac/bc: the lanes' 16 code bytes per fragment; asc/bsc: the lanes' two block
-// scales (bytes 0, 1) per fragment.
-template <int MF, int NF>
-__device__ __forceinline__ void dequant_step(int s, const uint4 (&ac)[MF], const uint32_t (&asc)[MF],
-                                             const uint4 (&bc)[NF], const uint32_t (&bsc)[NF], half8_t (&av)[MF],
-                                             half8_t (&bv)[NF]) {
-#pragma unroll
-  for (int i = 0; i < MF; ++i) {
-    const uint32_t cw = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
-    av[i] = dequant8(cw, scale_pair_f16(scale_byte(asc[i], s)));
-  }
-#pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    const uint32_t cw = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
-    bv[j] = dequant8(cw, scale_pair_f16(scale_byte(bsc[j], s)));
-  }
-}
-
-// As dequant_step, with whole scale dwords: the lane's pair starts at bit hsh.
-template <int MF, int NF>
-__device__ __forceinline__ void dequant_step_h(uint32_t hsh, int s, const uint4 (&ac)[MF], const uint32_t (&asc)[MF],
-                                               const uint4 (&bc)[NF], const uint32_t (&bsc)[NF], half8_t (&av)[MF],
-                                               half8_t (&bv)[NF]) {
-  const uint32_t off = hsh + 8u * (uint32_t)(s >> 1);
-#pragma unroll
-  for (int i = 0; i < MF; ++i) {
-    const uint32_t cw = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
-    av[i] = dequant8(cw, scale_pair_f16(__builtin_amdgcn_ubfe(asc[i], off, 8)));
-  }
-#pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    const uint32_t cw = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
-    bv[j] = dequant8(cw, scale_pair_f16(__builtin_amdgcn_ubfe(bsc[j], off, 8)));
-  }
-}
-
 // The lane's two scale pairs (blocks 2h and 2h+1 of a 64-wide K tile) of each
 // fragment as f16 pairs, computed once per K step: sub-steps 0, 1 use pair 0
 // and sub-steps 2, 3 pair 1.
@@ -658,7 +621,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU, bool PIPE>
+template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
                         const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
@@ -781,7 +744,6 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     return wave_n * NF + j;
   };
 
-if constexpr (PIPE) {
   // Software pipeline across K steps.  Within step kt the four 16-wide
   // sub-steps multiply operands that were dequantised during the previous
   // sub-step, so the VALU work issues in the MFMA shadow.  Between sub-steps
@@ -902,60 +864,6 @@ if constexpr (PIPE) {
       if (kt < KT) kstep(b, kt + 1 < KT, kt + NSTAGE < KT, std::integral_constant<int, 0>{});
     });
   }
-} else {
-  // One K step: wait for its stage, barrier, read the wave's fragments,
-  // optionally issue the DMA of stage kt+NSTAGE-1, multiply.
-  auto kstep = [&](auto b, int64_t kt, bool do_issue, auto waitn) __attribute__((always_inline)) {
-    constexpr int B = decltype(b)::value;
-    wait_vmcnt<decltype(waitn)::value>();
-    // A bare barrier (no memory fence): the DMA of this stage is covered by the
-    // vmcnt wait above, and the previous stage's LDS reads have all been
-    // consumed by that step's MFMAs, so no further waits are needed.
-    compiler_fence();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    const uint8_t* base = buf(b);
-    uint4 ac[MF], bc[NF];
-    uint32_t asc[MF], bsc[NF];
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int f = wave_m * MF + i;
-      ac[i] = *reinterpret_cast<const uint4*>(base + f * 1024 + lane * 16);
-      asc[i] = reinterpret_cast<const uint32_t*>(base + P::OFF_AS)[f * 32 + r] >> (16 * h);
-    }
-#pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      const int tl = lds_tile(j);
-      bc[j] = *reinterpret_cast<const uint4*>(base + P::OFF_BC + tl * 1024 + lane * 16);
-      bsc[j] = reinterpret_cast<const uint32_t*>(base + P::OFF_BS)[tl * 32 + r] >> (16 * h);
-    }
-    // The next stage's loads go out after this stage's reads are issued.
-    if (do_issue) issue(buf(std::integral_constant<int, (B + NSTAGE - 1) % NSTAGE>{}),
-                        std::integral_constant<int, (B + NSTAGE - 1) % NSTAGE>{});
-    mma_k64<MF, NF>(acc, ac, asc, bc, bsc);
-  };
-
-  // Prologue: stages 0..NSTAGE-2 (the launcher guarantees KT >= NSTAGE).
-  static_for<0, NSTAGE - 1>([&](auto s) __attribute__((always_inline)) { issue(buf(s), s); });
-  // Steady state, in groups of NSTAGE steps with compile-time buffers; every
-  // step issues, so the in-flight DMA pattern is the same at every step.
-  int64_t kt0 = 0;
-  for (; kt0 + 2 * NSTAGE - 2 < KT; kt0 += NSTAGE) {
-    static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
-      kstep(b, kt0 + decltype(b)::value, true, std::integral_constant<int, P::LPW * (NSTAGE - 2)>{});
-    });
-  }
-  // Tail: the last 2*NSTAGE-2 or fewer steps.  kt0 is a multiple of NSTAGE, so
-  // the buffers are again compile-time; loads are issued while stages remain
-  // and every step waits for all in-flight loads (a handful of steps).
-  for (; kt0 < KT; kt0 += NSTAGE) {
-    static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
-      const int64_t kt = kt0 + decltype(b)::value;
-      if (kt < KT) kstep(b, kt, kt + NSTAGE - 1 < KT, std::integral_constant<int, 0>{});
-    });
-  }
-
-}
 
   tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds_epi, ctab, lane, wave, wave_m, wave_n, m0,
                                       SILU ? o0 : (int64_t)bx * BN, m, n, out, epi);
@@ -1599,7 +1507,7 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
     const TileMap tail{(int)grid.x, (int)grid.y, (int)nbig, ry, rx, 0};
     const dim3 tail_grid((unsigned)(rem * ry * rx));
 #define NVFP4_LAUNCH_PIECE(MFP, NFP, SL, GRID, MAP) \
-  hipLaunchKernelGGL((gemm_prefill_dma_kernel<MFP, NFP, WM, WN, NS, SL, true>), GRID, block, 0, st, ac, as, m, w, n, \
+  hipLaunchKernelGGL((gemm_prefill_dma_kernel<MFP, NFP, WM, WN, NS, SL>), GRID, block, 0, st, ac, as, m, w, n, \
                      k, out, epi, MAP)
     if (epi.silu_mul) {
       NVFP4_LAUNCH_PIECE(MF, NF, true, dim3((unsigned)nbig), big);
