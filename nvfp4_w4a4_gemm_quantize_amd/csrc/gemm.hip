@@ -523,10 +523,12 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
 // n are not masked: their addresses are clamped to the last valid row/tile,
 // which keeps every wave's load count fixed (the vmcnt accounting below
 // relies on it) and only feeds output rows/columns that are never stored.
-// Loads for stage kt+NSTAGE-1 are issued right after the barrier of step kt,
-// into the buffer step kt-1 has finished with.
-// VALU ops issued after each MFMA in the pipelined main loop, and the MFMAs
-// of the last sub-step issued before any VALU op that needs the next stage.
+// In step kt, right after the barrier that publishes stage kt+1, the loads
+// for stage kt+NSTAGE go into buffer kt % NSTAGE, whose fragments every wave
+// has read before that barrier.
+// Tuning of the main loop's schedule: VALU ops issued after each MFMA, and
+// MFMAs of the last sub-step issued before any VALU op that needs the next
+// stage.
 #ifndef NVFP4_XPIPE
 #define NVFP4_XPIPE 5
 #endif
