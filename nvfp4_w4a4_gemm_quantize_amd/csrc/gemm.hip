@@ -191,6 +191,14 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
   };
 
   const float alpha_silu = SILU ? 1.0f / (ga * epi.seg_w_global[0]) : 0.0f;
+  // SiLU(gate) * up of a fragment pair, in the accumulator layout (the gate
+  // and up fragments share it), so only the result goes through LDS.
+  auto silu_frag = [&](const floatx16& g, const floatx16& u) __attribute__((always_inline)) -> floatx16 {
+    floatx16 hv;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) hv[e] = silu_mul(g[e] * alpha_silu, u[e] * alpha_silu);
+    return hv;
+  };
   // Quantising SiLU*mul: lane (r, h) takes row r, columns 16h..16h+15 of the
   // staged fragment -- one whole 16-element block of h.
   const bool quant = SILU && epi.h_codes != nullptr;
@@ -205,28 +213,20 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
     const int64_t col0 = col_base + c0;
     if constexpr (SILU) {
       if (quant) {
-        float gq[16], uq[16];
+        float hq[16];
         wave_lds_order();
         static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
           constexpr int F = decltype(c)::value;
-          if (f == F) stage_frag(acc[F % MF][F / MF]);
+          if (f == F) stage_frag(silu_frag(acc[F % MF][F / MF], acc[F % MF][F / MF + NF / 2]));
         });
         wave_lds_order();
-        read_block(gq);
-        wave_lds_order();
-        static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
-          constexpr int F = decltype(c)::value;
-          if (f == F) stage_frag(acc[F % MF][F / MF + NF / 2]);
-        });
-        wave_lds_order();
-        read_block(uq);
+        read_block(hq);
         // h rounded to bf16 first, then the quantiser's own block arithmetic:
         // the codes equal those of the bf16 h quantised on its own.
         uint32_t hb[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-          hb[c] = (uint32_t)f32_to_bf16_rne(silu_mul(gq[2 * c] * alpha_silu, uq[2 * c] * alpha_silu)) |
-                  ((uint32_t)f32_to_bf16_rne(silu_mul(gq[2 * c + 1] * alpha_silu, uq[2 * c + 1] * alpha_silu)) << 16);
+          hb[c] = (uint32_t)f32_to_bf16_rne(hq[2 * c]) | ((uint32_t)f32_to_bf16_rne(hq[2 * c + 1]) << 16);
         const uint4 lo = make_uint4(hb[0], hb[1], hb[2], hb[3]), hi = make_uint4(hb[4], hb[5], hb[6], hb[7]);
         uint2 codes;
         const uint32_t S = quantize_block16(lo, hi, hg, &codes);
@@ -249,24 +249,15 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
     wave_lds_order();
     static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
       constexpr int F = decltype(c)::value;
-      if (f == F) stage_frag(acc[F % MF][F / MF]);
+      if constexpr (SILU) {
+        if (f == F) stage_frag(silu_frag(acc[F % MF][F / MF], acc[F % MF][F / MF + NF / 2]));
+      } else {
+        if (f == F) stage_frag(acc[F % MF][F / MF]);
+      }
     });
     wave_lds_order();
     read_frag(v);
-    if constexpr (SILU) {
-      float u[4][4];
-      wave_lds_order();
-      static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
-        constexpr int F = decltype(c)::value;
-        if (f == F) stage_frag(acc[F % MF][F / MF + NF / 2]);
-      });
-      wave_lds_order();
-      read_frag(u);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v[a][b] = silu_mul(v[a][b] * alpha_silu, u[a][b] * alpha_silu);
-    } else {
+    if constexpr (!SILU) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const ColumnEpilogue ce = ctab[c0 + b];
