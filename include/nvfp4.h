@@ -105,6 +105,21 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                    uint8_t* codes, uint8_t* scales, nvfp4_stream_t stream);
 
 /*
+ * nvfp4_e2m1_encode -- the element encoder of nvfp4_quantize on its own, for
+ * verification: codes[i] = the 4-bit E2M1 code (0..15, one per byte) that the
+ * quantizer gives the scaled value q[i] (q = x * g / value(S) in the
+ * quantisation rule above): sign bit 3 = the sign bit of q[i] (-0 gives 8),
+ * magnitude rounded to the nearest of 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to
+ * the even code, magnitudes above 6 giving 6 (code 7).  NVFP4's element type
+ * (aipulsen page, second paragraph).
+ *
+ *   q      device float [n], 4-byte aligned; finite values (NaN unspecified).
+ *   n      >= 0 (0 enqueues nothing).
+ *   codes  device uint8 [n], out.
+ */
+int nvfp4_e2m1_encode(const float* q, int64_t n, uint8_t* codes, nvfp4_stream_t stream);
+
+/*
  * nvfp4_packed_weight_bytes -- bytes of the opaque packed weight buffer for
  * an [n, k] weight (k % 16 == 0); 0 for invalid sizes.  It is the NVFP4
  * storage (k/2 + k/16 bytes per row, i.e. 4.5 bits per weight) of the weight
@@ -150,7 +165,8 @@ int nvfp4_unpack_weights_linear(const void* packed, int64_t n, int64_t k,
  *   a_codes, a_scales  the activation as written by nvfp4_quantize for an
  *                      [m, k] tensor (contiguous).
  *   a_global, w_global device floats (encode-form global scales).
- *   m >= 0 (0 enqueues nothing), n >= 1, k >= 32, k % 32 == 0.
+ *   m >= 0 (0 enqueues nothing), n >= 1, k >= 16, k % 16 == 0 (any K that
+ *                      NVFP4 blocks divide).
  *   w_packed           from nvfp4_pack_weights with the same n, k.  A
  *                      weight packed with several segments is treated as one
  *                      module with scale *w_global (use the fused-segment
@@ -222,10 +238,11 @@ int gemm_w4a4_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
 
 /*
  * gdn_recurrence -- the gated delta-rule recurrence of a Gated DeltaNet layer,
- * the recurrent half that the in-projection feeds.  The pages describe it by
- * its mechanism: every write overwrites the state along the current key
- * direction, so injected noise plateaus and a state impulse is forgotten
- * (bayesiansapien page, "The four-part mechanism study", third item).  The
+ * the recurrent half that the in-projection feeds.  The pages characterise
+ * it by behaviour rather than by a formula: the delta rule replaces the
+ * state's component along the key, so errors do not pile up and an old
+ * disturbance fades (bayesiansapien page, "The four-part mechanism study",
+ * third item).  The
  * rule computed (the standard gated delta rule), per value head h with key
  * head h / (hv / hk) and fp32 state S [head_dim, head_dim] (row = value
  * index, column = key index), for t = 0 .. T-1:

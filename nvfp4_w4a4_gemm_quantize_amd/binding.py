@@ -28,6 +28,7 @@ _int = ctypes.c_int
 
 _SIGNATURES = {
     "nvfp4_quantize": (_int, [_c_p, _i64, _i64, _i64, _c_p, _int, _c_p, _c_p, _c_p]),
+    "nvfp4_e2m1_encode": (_int, [_c_p, _i64, _c_p, _c_p]),
     "nvfp4_packed_weight_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_pack_weights": (_int, [_c_p, _i64, _i64, _int, _c_p, _c_p, _int, _c_p, ctypes.c_size_t, _c_p]),
     "nvfp4_unpack_weights_linear": (_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
@@ -125,6 +126,22 @@ def nvfp4_quantize(x, global_scale=None, dynamic=True, codes=None, scales=None):
                             _ptr(codes), _ptr(scales), _stream())
     _check(rc, "nvfp4_quantize")
     return codes, scales, global_scale
+
+
+def nvfp4_e2m1_encode(q, codes=None):
+    """fp32 [n] -> E2M1 codes u8 [n] (0..15), through the quantizer's device encoder."""
+    lib = load()
+    _dev(q, torch.float32, "q")
+    if not q.is_contiguous():
+        raise NVFP4Error("q must be contiguous")
+    n = q.numel()
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _dev(codes, torch.uint8, "codes")
+    if codes.numel() < n or not codes.is_contiguous():
+        raise NVFP4Error("codes must be a contiguous uint8 buffer of at least n bytes")
+    _check(lib.nvfp4_e2m1_encode(_ptr(q), n, _ptr(codes), _stream()), "nvfp4_e2m1_encode")
+    return codes
 
 
 def nvfp4_packed_weight_bytes(n, k):

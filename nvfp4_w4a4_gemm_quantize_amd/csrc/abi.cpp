@@ -33,6 +33,12 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, 
                                     (hipStream_t)stream));
 }
 
+int nvfp4_e2m1_encode(const float* q, int64_t n, uint8_t* codes, nvfp4_stream_t stream) {
+  int rc = validate_e2m1_encode(q, n, codes);
+  if (rc || n == 0) return rc;
+  return hip_status(launch_e2m1_encode(q, n, codes, (hipStream_t)stream));
+}
+
 size_t nvfp4_packed_weight_bytes(int64_t n, int64_t k) { return packed_weight_bytes(n, k); }
 
 int nvfp4_pack_weights(const uint16_t* w, int64_t n, int64_t k, int num_segments, const int64_t* seg_offsets,

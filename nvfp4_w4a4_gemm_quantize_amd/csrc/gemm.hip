@@ -329,8 +329,11 @@ __device__ __forceinline__ void mma_k64(floatx16 (&acc)[MF][NF], const uint4 (&a
 }
 
 // --------------------------------------------- prefill kernel, any K ----
-// Register-staged variant for K % 64 == 32 (a half K tile at the end): every
-// load is guarded and zero-filled.  Workgroup tile BM x BN over the whole K;
+// Register-staged variant for K % 64 != 0 (a partial K tile at the end):
+// every load is guarded and zero-filled.  With K % 32 == 16 the rows of A's
+// codes are only 8-byte aligned and its scale rows have odd length, so A then
+// moves in 8-byte code halves (each 16-element block guarded on its own) and
+// single scale bytes.  Workgroup tile BM x BN over the whole K;
 // per 64-wide K step the packed A rows and W tiles go global -> registers ->
 // LDS (double buffered) and each wave multiplies its fragments.
 // SILU: the workgroup covers BN/2 output columns o0.. and loads the matching
@@ -376,7 +379,7 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
-  const bool k_aligned64 = (k & 63) == 0;
+  const bool k_aligned64 = (k & 63) == 0, k_aligned32 = (k & 31) == 0;
   const int64_t o0 = SILU ? (int64_t)blockIdx.x * (BN / 2) : 0;
   if constexpr (!SILU) fill_column_table<BN, NT>(ctab, epi, (int64_t)blockIdx.x * BN, n);
 
@@ -403,8 +406,16 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
     for (int i = 0; i < A_PER_T; ++i) {
       const int q = t + i * NT;
       const int row = q >> 1, hh = q & 1;
-      const bool ok = q < A_CHUNKS && (m0 + row) < m && (kt * 64 + hh * 32) < k;
-      ra[i] = ld16(a_codes + (m0 + row) * a_row_bytes + kt * 32 + hh * 16, ok);
+      const int64_t k0 = kt * 64 + hh * 32;
+      const bool ok = q < A_CHUNKS && (m0 + row) < m && k0 < k;
+      const uint8_t* p = a_codes + (m0 + row) * a_row_bytes + kt * 32 + hh * 16;
+      if (k_aligned32) {
+        ra[i] = ld16(p, ok);
+      } else {
+        const uint2 lo = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+        const uint2 hi = ok && k0 + 16 < k ? *reinterpret_cast<const uint2*>(p + 8) : make_uint2(0u, 0u);
+        ra[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
     }
 #pragma unroll
     for (int i = 0; i < AS_PER_T; ++i) {
@@ -414,9 +425,12 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
         const uint8_t* p = a_scales + (m0 + row) * a_row_scales + kt * 4;
         if (k_aligned64) {
           v = *reinterpret_cast<const uint32_t*>(p);
-        } else {
+        } else if (k_aligned32) {
           v = *reinterpret_cast<const uint16_t*>(p);
           if (kt * 64 + 32 < k) v |= (uint32_t)(*reinterpret_cast<const uint16_t*>(p + 2)) << 16;
+        } else {
+          for (int b = 0; b < 4; ++b)
+            if (kt * 64 + 16 * b < k) v |= (uint32_t)p[b] << (8 * b);
         }
       }
       ras[i] = v;
@@ -1282,9 +1296,11 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
   const bool a_on = amm < MR && h == (aq >> 1);
   const uint32_t a_lane = a_on ? (uint32_t)((aq * MR + amm) * 16) : (uint32_t)(4 * MR * 16);
 
-  // Partial sums per (slab, row[, block slot]): with one row per lane the four
-  // block slots get chains of their own, otherwise the rows are the chains.
-  constexpr int QC = MH == 1 ? 4 : 1;
+  // Partial sums per (slab, row, block slot): the four block slots of a tile
+  // feed four independent chains, so a chain adds one term per tile (K/64
+  // terms in all, split further over the waves) and its FP32 rounding stays
+  // far below the 1e-5 * sum|a*w| acceptance bound at any K that fits LDS.
+  constexpr int QC = 4;
   float y4[NS][MH][QC];
 #pragma unroll
   for (int j = 0; j < NS; ++j)
@@ -1446,17 +1462,13 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
 #define NVFP4_PREFILL_STAGES 4
 #endif
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (a host-side attribute query).
 static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 256;
+  return v;
 }
 
 template <int MF, int NF, int WM, int WN>
@@ -1472,7 +1484,10 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
   // wave-uniform base: A's codes must stay below 4 GiB (else the register-staged
   // kernel, with full 64-bit addresses, runs).
   const bool a_fits_32 = m * (k / 2) < ((int64_t)1 << 32) - 64;
-  if ((k & 63) == 0 && k / kTileK >= NS && a_fits_32) {
+  // ... and the two weight tiles of a scale-pair load differ by one slab
+  // (super_count(k) * kSuperBytes bytes), also a 32-bit per-lane offset.
+  const bool w_fits_32 = super_count(k) * kSuperBytes < ((int64_t)1 << 32) - 1024;
+  if ((k & 63) == 0 && k / kTileK >= NS && a_fits_32 && w_fits_32) {
     // One workgroup per CU at a time: when the last round would leave most
     // CUs idle, its tiles run as a second launch of smaller pieces -- each
     // tile cut into ry row bands and rx column bands, the finest cut whose
@@ -1602,7 +1617,9 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, in
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   if (m <= 4 && try_decode_fp4(a_codes, a_scales, m, w_packed, n, k, out, epi, st)) return hipGetLastError();
-  if (m <= 64) {
+  // The f16 decode kernel moves A in 16-byte chunks (32 elements): K % 32 == 16
+  // runs the register-staged tile kernel, which reads A per 16-element block.
+  if (m <= 64 && k % 32 == 0) {
     if (m <= 32) {
       if (epi.silu_mul) launch_decode<1, true>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
       else launch_decode<1, false>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);

@@ -42,6 +42,7 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_
                            bool dynamic, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const SegmentTable& segs, float* seg_g,
                        bool dynamic, uint8_t* packed, hipStream_t st);
+hipError_t launch_e2m1_encode(const float* q, int64_t n, uint8_t* codes, hipStream_t st);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
                          hipStream_t st);
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,

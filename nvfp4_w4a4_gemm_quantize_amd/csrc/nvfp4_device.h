@@ -53,14 +53,46 @@ __device__ __forceinline__ float e4m3_decode(uint32_t s) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// --------------------------------------------------------------- E2M1 ----
+// 4-bit E2M1 code of an FP32 value q: sign bit 3 (the sign of q, also for
+// -0), magnitude |q| rounded to the nearest of 0, .5, 1, 1.5, 2, 3, 4, 6 with
+// ties to the even code, and every magnitude above 6 giving 6.  Integer
+// arithmetic on the bit pattern, no conversion instruction:
+//   |q| < 1   the grid is uniform with step .5, so the code is rint(2|q|)
+//             (RNE; 2|q| is exact), i.e. 0, 1 or 2 (2 is the code of 1.0);
+//   |q| >= 1  the significand is rounded to one bit with ties to even, the
+//             carry moving into the exponent; the code is 2 + 2e + m for
+//             |q| = 2^e (1 + m/2), clamped to 7 (saturation).
+__device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float q) {
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t c;
+  if (a < 0x3F800000u) {
+    c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
+  } else {
+    const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+    c = min((r >> 22) - 252u, 7u);        // (biased exponent 127 + e) * 2 + m - 254 + 2
+  }
+  return c | ((b >> 28) & 8u);
+}
+
 // ---------------------------------------------------- block quantizer ----
 // Quantise 16 bf16 values (two uint4) with global scale g.  Writes 8 code
 // bytes (low nibble = even element) and returns the E4M3 scale byte.
 //   u = min((m/6)*g, 448); S = E4M3 RNE(u); S == 0 -> codes 0;
-//   r = g / value(S); code_i = fp4_rne_sat(x_i * r) with the sign of x_i.
-// Every step is one IEEE FP32 operation (correctly rounded division; the
-// hardware FP32 -> E2M1 conversion rounds to nearest even, saturates at 6
-// and keeps the sign, with a unit scale).
+//   r = g / value(S); code_i = E2M1 RNE, saturating, of x_i * r, with the sign of x_i.
+// Every step is one IEEE FP32 operation (correctly rounded division, a
+// correctly rounded product q = x_i * r) followed by the integer E2M1 encoder.
+__device__ __forceinline__ uint32_t pack_codes8(const uint32_t (&w)[4], float r) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c |= e2m1_encode_rne_sat(bf16_lo(w[i]) * r) << (8 * i);
+    c |= e2m1_encode_rne_sat(bf16_hi(w[i]) * r) << (8 * i + 4);
+  }
+  return c;
+}
+
 __device__ __forceinline__ uint32_t quantize_block16(uint4 lo, uint4 hi, float g, uint2* codes_out) {
   uint32_t mbits = max(absmax_bits8(lo), absmax_bits8(hi));
   float m = __uint_as_float(mbits << 16);
@@ -70,18 +102,9 @@ __device__ __forceinline__ uint32_t quantize_block16(uint4 lo, uint4 hi, float g
   uint2 c = make_uint2(0u, 0u);
   if (S != 0) {
     float r = g / e4m3_decode(S);
-    uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
-    uint32_t v[4] = {hi.x, hi.y, hi.z, hi.w};
-    uint32_t c0 = 0, c1 = 0;
-    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[0]) * r, bf16_hi(w[0]) * r, 1.0f, 0);
-    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[1]) * r, bf16_hi(w[1]) * r, 1.0f, 1);
-    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[2]) * r, bf16_hi(w[2]) * r, 1.0f, 2);
-    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, bf16_lo(w[3]) * r, bf16_hi(w[3]) * r, 1.0f, 3);
-    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[0]) * r, bf16_hi(v[0]) * r, 1.0f, 0);
-    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[1]) * r, bf16_hi(v[1]) * r, 1.0f, 1);
-    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[2]) * r, bf16_hi(v[2]) * r, 1.0f, 2);
-    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, bf16_lo(v[3]) * r, bf16_hi(v[3]) * r, 1.0f, 3);
-    c = make_uint2(c0, c1);
+    const uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
+    const uint32_t v[4] = {hi.x, hi.y, hi.z, hi.w};
+    c = make_uint2(pack_codes8(w, r), pack_codes8(v, r));
   }
   *codes_out = c;
   return S;

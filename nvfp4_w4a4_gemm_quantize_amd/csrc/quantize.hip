@@ -165,6 +165,15 @@ unpack_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int64_t 
   }
 }
 
+// ------------------------------------------------------ E2M1 encoder ----
+// The quantizer's E2M1 encoder applied to caller-given FP32 values, one code
+// (0..15) per byte: exposes the exact device routine for verification.
+__global__ void __launch_bounds__(kThreads)
+e2m1_encode_kernel(const float* __restrict__ q, int64_t n, uint8_t* __restrict__ codes) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    codes[i] = (uint8_t)e2m1_encode_rne_sat(q[i]);
+}
+
 // ---------------------------------------------------------- launchers ----
 static int grid_for(int64_t items, int64_t cap) {
   int64_t g = (items + kThreads - 1) / kThreads;
@@ -223,6 +232,11 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* c
   const int64_t np = round_up(n, kTileN), kp = round_up(k, kSuperK);
   hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(n * (k / 16), 16384)), dim3(kThreads), 0, st,
                      packed, n, k, np, kp, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_e2m1_encode(const float* q, int64_t n, uint8_t* codes, hipStream_t st) {
+  hipLaunchKernelGGL(e2m1_encode_kernel, dim3(grid_for(n, 8192)), dim3(kThreads), 0, st, q, n, codes);
   return hipGetLastError();
 }
 

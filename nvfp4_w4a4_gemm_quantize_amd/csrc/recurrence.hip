@@ -1,8 +1,8 @@
 // Gated delta-rule recurrence of a Gated DeltaNet layer on gfx950: the
 // second workload of the path, fed by the fused in-projection (its q, k, v
-// columns and the sigmoid / decay gate columns).  The pages describe the
-// rule by its behaviour -- each write overwrites the state along the current
-// key direction (bayesiansapien page, "The four-part mechanism study", third
+// columns and the sigmoid / decay gate columns).  The pages give the rule's
+// behaviour, not a formula -- a write replaces the state's component along
+// the key (bayesiansapien page, "The four-part mechanism study", third
 // item); per value head h, with key head h / (Hv / Hk) and state S [128, 128]
 // (row = value index, column = key index):
 //     k^ = k / sqrt(|k|^2 + 1e-6),  q^ likewise,  alpha = exp(g),

@@ -18,6 +18,14 @@ int validate_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, c
   return NVFP4_OK;
 }
 
+int validate_e2m1_encode(const void* q, int64_t n, const void* codes) {
+  if (n < 0) return NVFP4_ESHAPE;
+  if (n == 0) return NVFP4_OK;
+  if (!q || !codes) return NVFP4_EINVAL;
+  if (reinterpret_cast<uintptr_t>(q) & 3u) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
 size_t packed_weight_bytes(int64_t n, int64_t k) {
   if (n <= 0 || k <= 0 || k % 16 != 0) return 0;
   const int64_t np = (n + 31) / 32 * 32, kp = (k + 255) / 256 * 256;   // 32-row slabs, 256-wide super-tiles
@@ -54,8 +62,7 @@ int validate_unpack(const void* packed, int64_t n, int64_t k, const void* codes,
 int validate_gemm_common(const void* a_codes, const void* a_scales, const void* a_global, int64_t m,
                          const void* w_packed, int64_t n, int64_t k, const void* out, int out_dtype,
                          int64_t ld_out, int64_t out_cols) {
-  if (m < 0 || n <= 0 || k <= 0) return NVFP4_ESHAPE;
-  if (k % 32 != 0) return k % 16 == 0 ? NVFP4_EUNSUPPORTED : NVFP4_ESHAPE;
+  if (m < 0 || n <= 0 || k <= 0 || k % 16 != 0) return NVFP4_ESHAPE;
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_EINVAL;
   if (ld_out < out_cols) return NVFP4_ESHAPE;
   if (m == 0) return NVFP4_OK;
@@ -71,8 +78,7 @@ int validate_gemm_silu_quantize(const void* a_codes, const void* a_scales, const
                                 const void* w_packed, const void* w_global, int64_t n, int64_t k,
                                 const void* h_global, const void* h_codes, const void* h_scales,
                                 const void* h_out) {
-  if (m < 0 || n <= 0 || k <= 0 || n % 64 != 0) return NVFP4_ESHAPE;
-  if (k % 32 != 0) return k % 16 == 0 ? NVFP4_EUNSUPPORTED : NVFP4_ESHAPE;
+  if (m < 0 || n <= 0 || k <= 0 || k % 16 != 0 || n % 64 != 0) return NVFP4_ESHAPE;
   if (m == 0) return NVFP4_OK;
   if (!a_codes || !a_scales || !a_global || !w_packed || !w_global || !h_global || !h_codes || !h_scales)
     return NVFP4_EINVAL;

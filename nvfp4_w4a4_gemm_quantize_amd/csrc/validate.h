@@ -8,6 +8,7 @@ namespace nvfp4 {
 
 int validate_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const void* global_scale,
                       const void* codes, const void* scales);
+int validate_e2m1_encode(const void* q, int64_t n, const void* codes);
 size_t packed_weight_bytes(int64_t n, int64_t k);
 int validate_segments(int num_segments, const int64_t* seg_offsets, int64_t extent);
 int validate_pack(const void* w, int64_t n, int64_t k, int num_segments, const int64_t* seg_offsets,

@@ -1,14 +1,15 @@
 """Gated delta-rule recurrence of a Gated DeltaNet layer, in fp64 -- TEST
 INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-The pages describe the recurrence by its behaviour, not by a formula: every
-write overwrites the recurrent state along the current key direction, so the
-state is a continually overwritten register rather than an accumulator;
-injected noise stays at a flat plateau over 32K tokens and a state impulse is
-forgotten within hundreds of steps (bayesiansapien page, "The four-part
-mechanism study", third item; nefut page, third bullet; aimodeling page,
-"Why the recurrent half survives").  Their gates are the sigmoid write
-strength and the softplus/exponential decay of the same study's second item.
+The pages characterise the recurrence by its behaviour, not by a formula:
+the delta rule replaces the state's component along the current key instead
+of adding to it, which is why, in their measurements, the output error under
+injected noise levels off rather than growing with sequence length, and a
+disturbance of the state fades after some hundreds of steps
+(bayesiansapien page, "The four-part mechanism study", third item; nefut
+page, third bullet; aimodeling page, "Why the recurrent half survives").
+Their gates are the sigmoid write strength and the softplus/exponential
+decay of the same study's second item.
 
 Reading taken (the standard gated delta rule those words describe), per value
 head h with key head hk(h) = h // (Hv / Hk), state S [d_v, d_k] (row = value
@@ -44,12 +45,13 @@ def key_head_of(hv, hk):
     return np.arange(hv) // (hv // hk)
 
 
-def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False, return_row_l1=False):
+def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False, return_row_norms=False):
     """Run the gated delta rule.
 
     q, k  [T, Hk, d_k]; v [T, Hv, d_v]; beta, g [T, Hv]; s_init [Hv, d_v, d_k] or None (zeros).
     Returns (o [T, Hv, d_v], S_final [Hv, d_v, d_k]) and, with return_states, the list of states;
-    with return_row_l1 (instead), the row L1 norms sum_j |S_t[h, i, j]| [T, Hv, d_v] after each step.
+    with return_row_norms (instead), the L2 norms of the state rows, [T + 1, Hv, d_v]: entry 0 for
+    the initial state, entry t + 1 after step t.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -62,7 +64,9 @@ def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False, retu
     S = np.zeros((hv, dv, dk)) if s_init is None else np.array(s_init, dtype=np.float64)
     o = np.empty((T, hv, dv))
     states = []
-    row_l1 = np.empty((T, hv, dv)) if return_row_l1 else None
+    norms = np.empty((T + 1, hv, dv)) if return_row_norms else None
+    if return_row_norms:
+        norms[0] = np.linalg.norm(S, axis=2)
     for t in range(T):
         kn = l2_normalize(k[t], eps)[kh]                  # [Hv, d_k]
         qn = l2_normalize(q[t], eps)[kh]
@@ -73,35 +77,69 @@ def recurrence(q, k, v, beta, g, s_init=None, eps=EPS, return_states=False, retu
         o[t] = np.einsum("hij,hj->hi", S, qn)
         if return_states:
             states.append(S.copy())
-        if return_row_l1:
-            row_l1[t] = np.sum(np.abs(S), axis=2)
+        if return_row_norms:
+            norms[t + 1] = np.linalg.norm(S, axis=2)
     if return_states:
         return o, S, states
-    return (o, S, row_l1) if return_row_l1 else (o, S)
+    return (o, S, norms) if return_row_norms else (o, S)
 
 
-def fp32_tolerance(row_l1, v, s_init=None, out_is_bf16=False, o_ref=None):
-    """Per-element bound for an fp32 evaluation of the recurrence, [T, Hv, d_v].
+U32 = 2.0 ** -24          # unit roundoff of fp32 (round to nearest)
+U_BF16 = 2.0 ** -8        # unit roundoff of bf16 (8 significand bits)
 
-    Each step forms two 128-term dot products of a state row (with a key and a
-    query of norm <= 1) and one multiply-add per element; with unit roundoff
-    u = 2^-24 the error it adds to row i is at most c u (|S_i|_1 + |v_i|), with
-    c = 64 covering the dot-product length's rounding (the key's and query's own
-    normalisation errors included), and earlier errors are not amplified
-    because every step's map S -> alpha S (I - beta k^ k^T) has norm <= 1.  So
-    after t + 1 steps |o_t,i - o~| <= (t + 1) c u max_{tau <= t}(|S_tau,i|_1 + |v_tau,i|),
-    plus the state's initial magnitude, plus the bf16 rounding of the output
-    when it is bf16 (unit roundoff 2^-8: 8 significand bits, round to nearest).
-    """
-    u = 2.0 ** -24
-    T = row_l1.shape[0]
-    m = np.maximum.accumulate(row_l1 + np.abs(np.asarray(v, dtype=np.float64)), axis=0)
-    if s_init is not None:
-        m = np.maximum(m, np.sum(np.abs(np.asarray(s_init, dtype=np.float64)), axis=2)[None])
-    tol = (np.arange(1, T + 1, dtype=np.float64)[:, None, None]) * 64 * u * m
+
+def fp32_state_error_bound(row_norms, v, g, d=128):
+    """Bound on the error an fp32 evaluation of the recurrence can have in each
+    state row: E [T, Hv, d_v], E[t, h, i] >= || S~_t[h, i, :] - S_t[h, i, :] ||_2
+    after step t, for any order of the additions inside each step.
+
+    Error analysis of one step (unit roundoff u, row i, a = exp(g_t), state row
+    norms N = ||S_{t-1,i}||_2, value v_i; standard bounds: a d-term dot product in
+    any summation order is within d u sum|x_j y_j| <= d u ||x|| ||y|| of the exact
+    one, and the computed unit key k~ is within (d/2 + 4) u of the exact one,
+    the sum of its d squares, the square root and the division included):
+      - the state row times the key:        (d + d/2 + 5) u a N
+      - decay, write coefficient, the outer product and the add, per element a
+        few roundings of terms bounded by a|S_ij| and |v_i - u_i| |k_j|:
+                                             3 u (2 a N + |v_i|)
+      - the write's direction k~ - k^:      (d/2 + 4) u (|v_i| + a N)
+    so the step adds at most c u (a N + |v_i|) with c = 2 d + 20.  The error
+    already in the row is carried to the next step by x -> a x (I - beta k^ k^T),
+    whose norm is at most a for beta in [0, 1] and a unit key, so
+        E_t = a_t E_{t-1} + c u (a_t N_{t-1} + |v_t,i|),   E_{-1} = 0
+    (the initial state is given in fp32, exactly).  Norms are those of the exact
+    state; the difference to the computed state's is second order and covered by
+    a 1% margin."""
+    row_norms = np.asarray(row_norms, dtype=np.float64)
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    a = np.exp(np.asarray(g, dtype=np.float64))[:, :, None]          # [T, Hv, 1]
+    c = 2 * d + 20
+    T = v.shape[0]
+    E = np.empty_like(v)
+    e = np.zeros(v.shape[1:])
+    for t in range(T):
+        e = a[t] * e + c * U32 * (a[t] * row_norms[t] + v[t])
+        E[t] = e
+    return 1.01 * E
+
+
+def fp32_tolerance(row_norms, v, g, out_is_bf16=False, o_ref=None, d=128):
+    """Per-element bound for the outputs o_t = S_t q^ of an fp32 evaluation, [T, Hv, d_v]:
+    the state row's error (fp32_state_error_bound; |q^| <= 1) plus the output dot
+    product and the query's normalisation, (d + d/2 + 5) u ||S_t,i||_2, plus, for a
+    bf16 output, its rounding (unit roundoff 2^-8)."""
+    E = fp32_state_error_bound(row_norms, v, g, d)
+    tol = E + 1.01 * (d + d // 2 + 5) * U32 * np.asarray(row_norms, dtype=np.float64)[1:]
     if out_is_bf16:
-        tol = tol + 2.0 ** -8 * (np.abs(o_ref) + tol)
+        tol = tol + U_BF16 * (np.abs(o_ref) + tol)
     return tol
+
+
+def fp32_state_tolerance(row_norms, v, g, d=128):
+    """Per-element bound for the final state of an fp32 evaluation, [Hv, d_v, d_k]
+    (an element's error is at most its row's L2 error)."""
+    E = fp32_state_error_bound(row_norms, v, g, d)[-1]
+    return np.repeat(E[:, :, None], d, axis=2)
 
 
 def step_matrix_form(S, q, k, v, beta, g, eps=EPS):

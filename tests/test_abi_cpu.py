@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_four_entry_points_and_helpers():
     fns = declared_functions()
-    for name in ("nvfp4_quantize", "nvfp4_pack_weights", "gemm_w4a4", "gemm_w4a4_fused_segments",
+    for name in ("nvfp4_quantize", "nvfp4_e2m1_encode", "nvfp4_pack_weights", "gemm_w4a4", "gemm_w4a4_fused_segments",
                  "gemm_w4a4_silu_mul_quantize", "gdn_recurrence", "nvfp4_packed_weight_bytes",
                  "nvfp4_unpack_weights_linear",
                  "nvfp4_status_string", "nvfp4_last_hip_error"):
@@ -106,12 +106,22 @@ def test_pack_validation(lib):
     assert lib.nvfp4_pack_weights(A16, 64, 128, 1, None, A16, 1, A16, 9000, None) == EINVAL
 
 
+def test_e2m1_encode_validation(lib):
+    f = lib.nvfp4_e2m1_encode
+    assert f(A16, -1, A16, None) == ESHAPE
+    assert f(None, 0, None, None) == OK              # nothing to do
+    assert f(None, 8, A16, None) == EINVAL
+    assert f(A16, 8, None, None) == EINVAL
+    assert f(0x10002, 8, A16, None) == EALIGN        # fp32 input must be 4-byte aligned
+
+
 def gm(lib, ac=A16, asc=A16, ag=A16, m=64, w=A16, wg=A16, n=128, k=128, out=A16, dt=1, ld=128, epi=0):
     return lib.gemm_w4a4(ac, asc, ag, m, w, wg, n, k, out, dt, ld, epi, None)
 
 
 def test_gemm_validation(lib):
-    assert gm(lib, k=48) == EUNSUPPORTED       # a valid NVFP4 K (16 | K) the library does not run
+    assert gm(lib, k=48, ac=None) == EINVAL    # K = 48 (16 | K) passes the shape rule: the null pointer is caught
+    assert gm(lib, k=16, out=None) == EINVAL   # so does the smallest K
     assert gm(lib, k=40) == ESHAPE
     assert gm(lib, n=0) == ESHAPE
     assert gm(lib, m=-3) == ESHAPE
@@ -142,7 +152,8 @@ def test_fused_segments_validation(lib):
     assert fs(lib, epis=(0, 2), alog=None) == EINVAL
     assert fs(lib, sg=None) == EINVAL
     assert fs(lib, nseg=0, offs=(0,), epis=(0,)) == EINVAL
-    assert fs(lib, k=80) == EUNSUPPORTED
+    assert fs(lib, k=80, sg=None) == EINVAL     # K = 80 is a valid shape
+    assert fs(lib, k=72) == ESHAPE
     assert fs(lib, m=0, sg=None) == OK
 
 
@@ -154,7 +165,7 @@ def test_silu_mul_quantize_validation(lib):
     assert sq(lib, n=96) == ESHAPE              # gate/up halves of whole 32-column fragments: n % 64
     assert sq(lib, n=0) == ESHAPE
     assert sq(lib, m=-1) == ESHAPE
-    assert sq(lib, k=48) == EUNSUPPORTED
+    assert sq(lib, k=48, hc=None) == EINVAL     # K = 48 is a valid shape
     assert sq(lib, k=40) == ESHAPE
     assert sq(lib, hg=None) == EINVAL           # the static scale of h is required
     assert sq(lib, hc=None) == EINVAL
@@ -191,6 +202,30 @@ def test_gdn_recurrence_validation(lib):
     assert rec(lib, si=MIS) == EALIGN
     assert rec(lib, out=0x10002, dt=0) == EALIGN
     assert rec(lib, T=0, q=None, out=None) == OK
+
+
+def test_abi_layer_under_address_and_ub_sanitizers(tmp_path):
+    """abi.cpp and validate.cpp built for the host alone with ASan and UBSan,
+    driven by tests/abi_host_check.cpp (launchers stubbed): every status code
+    and the arguments that reach the launchers, with no sanitizer report."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    csrc = os.path.join(root, "nvfp4_w4a4_gemm_quantize_amd", "csrc")
+    exe = str(tmp_path / "abi_host_check")
+    cmd = [gxx, "-std=c++17", "-g", "-O1", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           os.path.join(root, "tests", "abi_host_check.cpp"), os.path.join(csrc, "abi.cpp"),
+           os.path.join(csrc, "validate.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0 and "cases ok" in r.stdout, r.stdout + r.stderr[-4000:]
+    assert "runtime error" not in r.stderr and "Sanitizer" not in r.stderr, r.stderr[-4000:]
 
 
 def test_binding_refuses_cpu_tensors():

@@ -6,6 +6,8 @@ GEMM).  Acceptance per element: |y_gpu - y| <= 1e-5 * sum_k |a_k w_k| * alpha
 (+ bf16 output rounding), bit-exact where the GEMM is an exact small-integer
 product, and Lipschitz-propagated bounds through the epilogues.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -99,6 +101,104 @@ def test_gemm_matches_oracle_everywhere(gpu_lib, M, N, K, out):
     ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits)
     yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
     check_gemm(gpu_out_f64(y), yr, br, out == "bf16", "gemm %dx%dx%d" % (M, N, K))
+
+
+@functools.lru_cache(maxsize=1)
+def decode_weight_prepared():
+    """The decode weight [17408, 5120], its oracle codes/scales/global scale."""
+    w_bits = inputs.decode(1)["W"]
+    g = OQ.dynamic_global_scale(w_bits)
+    cw, sw = oracle_quantize_rows(w_bits, g)
+    return w_bits, cw, sw, np.float32(g)
+
+
+# The FP4-MFMA decode kernel (m <= 4) and the branches around it: two and four
+# rows per MFMA (m = 2: the second row of the two-row kernel is stored; m = 3, 4:
+# the four-row kernel), the general A staging loop (more A records than the
+# unrolled staging covers: m = 3, 4 at K = 5120, m <= 2 at K >= 8192), and the
+# f16 decode kernel that takes over when the A records exceed the LDS budget.
+@pytest.mark.parametrize("M,N,K,out", [
+    (2, 17408, 5120, "bf16"), (3, 17408, 5120, "bf16"), (4, 17408, 5120, "bf16"),   # the decode config's W
+    (2, 1000, 5120, "f32"), (3, 1000, 5120, "f32"), (4, 1000, 5120, "f32"),         # ragged N
+    (1, 5120, 17408, "f32"), (2, 5120, 17408, "bf16"),     # K = 17408: general staging loop, 2-row kernel
+    (1, 96, 8192, "f32"), (2, 200, 9216, "f32"),
+    (3, 640, 17408, "f32"), (4, 640, 17408, "bf16"),       # 4-row records exceed LDS: f16 decode kernel
+])
+def test_small_m_decode_paths(gpu_lib, M, N, K, out):
+    rng = np.random.default_rng(M * 7919 + N + K)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[:, rng.choice(K, 5, replace=False)] *= 50
+    a_bits = inputs.f32_to_bf16_bits(a)
+    if (N, K) == (17408, 5120):
+        w_bits, cw, sw, gw = decode_weight_prepared()
+        gs = np.array([gw], np.float32)
+    else:
+        w_bits = inputs.f32_to_bf16_bits((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
+        gw = OQ.dynamic_global_scale(w_bits)
+        cw, sw = oracle_quantize_rows(w_bits, gw)
+        gs = np.array([gw], np.float32)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits)
+    assert np.float32(host(wg)[0]) == gs[0]
+    y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K,
+                          out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    ca, sa, ga = OQ.quantize(a_bits)
+    yr, br = oracle_gemm_rows(ca, sa, ga, cw, sw, OG.column_global(N, [0, N], gs))
+    check_gemm(gpu_out_f64(y), yr, br, out == "bf16", "decode %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_fused_segments_small_m_long_k(gpu_lib, M):
+    """Fused segments with sigmoid and decay gates through the FP4-MFMA decode
+    kernel at m = 2..4 and K = 5120, over a ragged N with six modules."""
+    rng = np.random.default_rng(500 + M)
+    K = 5120
+    widths = [256, 256, 384, 96, 48, 48]
+    offs = list(np.cumsum([0] + widths))
+    N = offs[-1]
+    f = [1.0, 8.0, 2.0, 4.0, 1.5, 3.0]
+    w = np.concatenate([rng.standard_normal((n, K)) * fs / np.sqrt(K) for n, fs in zip(widths, f)]).astype(np.float32)
+    a = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    a[:, rng.choice(K, 5, replace=False)] *= 50
+    a_bits, w_bits = inputs.f32_to_bf16_bits(a), inputs.f32_to_bf16_bits(w)
+    a_log = (rng.standard_normal(48) * 0.5).astype(np.float32)
+    dt = (rng.standard_normal(48) * 0.5).astype(np.float32)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits, offs)
+    epis = ["none", "none", "none", "none", "sigmoid", "gdn_decay"]
+    y = gpu_lib.gemm_w4a4_fused_segments(ac, asc, ag, packed, N, K, offs, wg, epis, f32(a_log), f32(dt),
+                                         out_dtype=torch.bfloat16)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits, offs)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    ref, tol = gdn_reference(yr, br, offs, a_log, dt)
+    assert_within(gpu_out_f64(y), ref, tol, "fused segments M=%d K=%d" % (M, K))
+
+
+# K = 16 (mod 32): a valid NVFP4 K whose last 32-element half holds one block.
+@pytest.mark.parametrize("M,N,K", [(1, 96, 48), (3, 64, 80), (8, 100, 48), (20, 256, 5136), (100, 96, 80),
+                                   (300, 160, 5136), (2, 512, 5136)])
+def test_k_odd_multiple_of_16(gpu_lib, M, N, K):
+    rng = np.random.default_rng(M * 31 + K)
+    a = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    a_bits, w_bits = inputs.f32_to_bf16_bits(a), inputs.f32_to_bf16_bits(w)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.float32)
+    check_gemm(gpu_out_f64(y), yr, br, False, "gemm %dx%dx%d" % (M, N, K))
+    # the fused-segment entry point with a gate, and SiLU*mul (n % 64 == 0), at the same K
+    offs = [0, N // 2, N]
+    y2 = gpu_lib.gemm_w4a4_fused_segments(ac, asc, ag, packed, N, K, offs, wg.repeat(2), ["none", "sigmoid"],
+                                          out_dtype=torch.float32)
+    ref, tol = yr.copy(), OG.tolerance(br, yr, False)
+    c = slice(N // 2, N)
+    ref[:, c], tol[:, c] = OE.sigmoid(yr[:, c]), OE.sigmoid_tolerance(yr[:, c], OG.GEMM_REL_TOL * br[:, c], False)
+    assert_within(gpu_out_f64(y2), ref, tol, "fused segments %dx%dx%d" % (M, N, K))
+    if N % 64 == 0:
+        h = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K, out_dtype=torch.float32, epilogue="silu_mul")
+        g_, u_ = yr[:, :N // 2], yr[:, N // 2:]
+        tol_h = OE.silu_mul_tolerance(g_, u_, OG.GEMM_REL_TOL * br[:, :N // 2], OG.GEMM_REL_TOL * br[:, N // 2:],
+                                      False)
+        assert_within(gpu_out_f64(h), OE.silu_mul(g_, u_), tol_h, "silu_mul %dx%dx%d" % (M, N, K))
 
 
 def test_tiny_workload(gpu_lib):
@@ -223,7 +323,7 @@ def test_single_alpha_negative_control(gpu_lib):
             assert not np.all(np.abs(yo[:, c] - yr[:, c]) <= OG.tolerance(br[:, c], yr[:, c], False))
 
 
-@pytest.mark.parametrize("M", [1, 48, 200])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 48, 200])
 def test_fused_segments_small(gpu_lib, M):
     """Fused segments on small shapes, whole output compared, both kernels."""
     rng = np.random.default_rng(M)

@@ -41,6 +41,34 @@ def test_golden_blocks(gpu_lib, case):
     assert g == case["g_expected"]
 
 
+# The seven E2M1 decision points (midpoints between neighbouring magnitudes).
+E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def _fp32_neighbourhood(x, span):
+    """Every fp32 value within `span` ulps of the positive value x."""
+    b = int(np.float32(x).view(np.uint32))
+    return np.arange(b - span, b + span + 1, dtype=np.int64).astype(np.uint32).view(np.float32)
+
+
+def test_e2m1_encoder_around_every_decision_point(gpu_lib):
+    """The device E2M1 encoder (the one the quantizer applies to x * g / s)
+    against the oracle's closed form (pinned exhaustively on the CPU): every fp32
+    within 2^16 ulps of each decision point, within 2^12 ulps of each grid value
+    and of 8, a strided sweep over all finite non-negative fp32 patterns
+    (subnormals to the largest finite), each with both signs (-0 included)."""
+    from oracle import formats as F
+    parts = [_fp32_neighbourhood(p, 1 << 16) for p in E2M1_MIDPOINTS]
+    parts += [_fp32_neighbourhood(p, 1 << 12) for p in (0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 8.0)]
+    parts.append(np.arange(0, 0x7F800000, 4099, dtype=np.uint32).view(np.float32))
+    parts.append(np.array([0, 1, 2, 0x007FFFFF, 0x00800000, 0x3E7FFFFF, 0x7F7FFFFF], np.uint32).view(np.float32))
+    mag = np.concatenate(parts)
+    q = np.concatenate([mag, -mag])
+    got = host(gpu_lib.nvfp4_e2m1_encode(torch.from_numpy(q).cuda()))
+    want = F.e2m1_rne_sat(np.abs(q)) | (np.signbit(q).astype(np.uint8) << 3)
+    assert_bytes_equal(got, want, "E2M1 encoder (%d values)" % q.size)
+
+
 ACTIVATIONS = {
     "tiny": lambda: inputs.tiny()["A"],
     "linear": lambda: inputs.linear()["A"],

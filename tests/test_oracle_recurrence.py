@@ -96,3 +96,75 @@ def test_key_head_mapping():
     np.testing.assert_array_equal(R.key_head_of(48, 16)[:7], [0, 0, 0, 1, 1, 1, 2])
     with pytest.raises(ValueError):
         R.key_head_of(10, 4)
+
+
+def _fp32_recurrence(q, k, v, beta, g, mistake=None):
+    """The gated delta rule evaluated in float32 throughout (numpy), written
+    independently of the fp64 oracle, optionally with a planted mistake:
+    "read_before_decay" takes S k^ on the undecayed state, "bf16_state" keeps the
+    state in bf16 between steps."""
+    T, hk, d = k.shape
+    hv = v.shape[1]
+    kh = np.arange(hv) // (hv // hk)
+    f = np.float32
+    q, k, v, beta, g = (np.asarray(x, dtype=f) for x in (q, k, v, beta, g))
+    S = np.zeros((hv, d, d), f)
+    o = np.empty((T, hv, d), f)
+    eps = f(1e-6)
+    for t in range(T):
+        kn = (k[t] / np.sqrt(np.sum(k[t] * k[t], axis=-1, keepdims=True) + eps))[kh]
+        qn = (q[t] / np.sqrt(np.sum(q[t] * q[t], axis=-1, keepdims=True) + eps))[kh]
+        a = np.exp(g[t])[:, None, None]
+        if mistake == "read_before_decay":
+            u = np.einsum("hij,hj->hi", S, kn)
+            S = a * S
+        else:
+            S = a * S
+            u = np.einsum("hij,hj->hi", S, kn)
+        S = S + (beta[t][:, None, None] * (v[t] - u)[:, :, None]) * kn[:, None, :]
+        if mistake == "bf16_state":
+            S = (S.view(np.uint32) + np.uint32(0x7FFF) + ((S.view(np.uint32) >> 16) & 1) & np.uint32(0xFFFF0000)).view(f)
+        o[t] = np.einsum("hij,hj->hi", S, qn)
+    return o, S
+
+
+def test_fp32_bound_holds_at_4096_steps_and_rejects_plausible_mistakes():
+    """Pin of fp32_tolerance / fp32_state_tolerance: an fp32 evaluation over 4096
+    steps (gates drawn as in the recurrence workload) stays inside the bound, with
+    the most-used element at more than 1/2000 of its tolerance (the bound takes
+    the worst case of every dot product, d u, where rounding errors typically
+    cancel to about sqrt(d) u / 2), while two plausible slips -- the key read on
+    the undecayed state, and a bf16 state between steps -- exceed it."""
+    from nvfp4_w4a4_gemm_quantize_amd import inputs
+    T, hk, hv, d = 4096, 1, 3, 128
+    raw = inputs.recurrence(T, hk, hv, seed=5)
+    f = lambda b: inputs.bf16_bits_to_f32(b).astype(np.float64)
+    q, k = f(raw["q"]).reshape(T, hk, d), f(raw["k"]).reshape(T, hk, d)
+    v, beta, g = f(raw["v"]).reshape(T, hv, d), f(raw["beta"]), f(raw["g"])
+    o, S, nr = R.recurrence(q, k, v, beta, g, return_row_norms=True)
+    tol, tol_s = R.fp32_tolerance(nr, v, g), R.fp32_state_tolerance(nr, v, g)
+    o32, S32 = _fp32_recurrence(q, k, v, beta, g)
+    use = np.abs(o32 - o) / tol
+    assert use.max() <= 1.0
+    assert use.max() > 1.0 / 2000, use.max()
+    assert np.all(np.abs(S32 - S) <= tol_s)
+    assert np.linalg.norm(o32 - o) <= 1e-5 * np.linalg.norm(o)
+    for mistake in ("read_before_decay", "bf16_state"):
+        om, _ = _fp32_recurrence(q, k, v, beta, g, mistake)
+        assert np.max(np.abs(om - o) / tol) > 2.0, mistake
+
+
+def test_fp32_bound_is_decay_damped():
+    """With every decay 1/2 an old error is halved each step, so the state bound
+    settles at c u (N + |v|) / (1 - 1/2) scale instead of growing with T."""
+    T, hv, d = 200, 1, 128
+    nr = np.ones((T + 1, hv, 4))
+    v = np.ones((T, hv, 4))
+    g = np.full((T, hv), np.log(0.5))
+    E = R.fp32_state_error_bound(nr, v, g, d)
+    c = 2 * d + 20
+    np.testing.assert_allclose(E[-1], 1.01 * c * R.U32 * (0.5 + 1) / (1 - 0.5), rtol=1e-12)
+    np.testing.assert_allclose(E[0], 1.01 * c * R.U32 * (0.5 + 1), rtol=1e-12)
+    # no decay: the bound grows linearly, one step's worth per step
+    E1 = R.fp32_state_error_bound(nr, v, np.zeros((T, hv)), d)
+    np.testing.assert_allclose(E1[-1], 1.01 * c * R.U32 * 2 * T, rtol=1e-12)
