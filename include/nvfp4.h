@@ -186,6 +186,30 @@ int gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gl
               void* out, int out_dtype, int64_t ld_out, int epilogue, nvfp4_stream_t stream);
 
 /*
+ * nvfp4_linear -- the whole W4A4 linear layer on a bf16 activation: the
+ * on-the-fly quantisation of x ("A4"; bayesiansapien page, TL;DR), with the
+ * same result bytes as nvfp4_quantize, which it also writes out, followed by
+ * gemm_w4a4 on those codes.  Decode-sized calls (m <= 2, epilogue NONE,
+ * k <= 6144) run as ONE kernel: every
+ * workgroup computes the activation's amax and global scale and quantises
+ * the (small) activation itself while its weight stream is in flight, and
+ * workgroup 0 writes the codes, scales and global scale; the output is then
+ * bit-identical to nvfp4_quantize + gemm_w4a4.  Other shapes enqueue those
+ * two calls.
+ *
+ *   x, m, k, ld_x   the activation: bf16 [m, k] as nvfp4_quantize's x, rows,
+ *                   cols, ld_x (k % 16 == 0, ld_x % 8 == 0).
+ *   a_global, dynamic_global   as nvfp4_quantize's global_scale and
+ *                   dynamic_global (written when dynamic, else read).
+ *   a_codes, a_scales  out: the quantised activation, [m, k/2] and [m, k/16]
+ *                   bytes, contiguous (codes 16-byte aligned).
+ *   w_packed, w_global, n, out, out_dtype, ld_out, epilogue   as gemm_w4a4.
+ */
+int nvfp4_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x, float* a_global, int dynamic_global,
+                 uint8_t* a_codes, uint8_t* a_scales, const void* w_packed, const float* w_global, int64_t n,
+                 void* out, int out_dtype, int64_t ld_out, int epilogue, nvfp4_stream_t stream);
+
+/*
  * gemm_w4a4_fused_segments -- one GEMM over a fused weight whose column
  * segments are separately calibrated modules: the global-scale-mismatch
  * repair of the bayesiansapien page ("Two practical repairs") and aimodeling
@@ -268,6 +292,20 @@ int gdn_recurrence(const uint16_t* q, int64_t ld_q, const uint16_t* k, int64_t l
                    int64_t ld_v, const uint16_t* beta, int64_t ld_beta, const uint16_t* g, int64_t ld_g,
                    int64_t T, int hk, int hv, int head_dim, const float* s_init, float* s_final, void* out,
                    int out_dtype, int64_t ld_out, nvfp4_stream_t stream);
+
+/*
+ * nvfp4_weight_stream_read -- measurement reference for the decode GEMMs,
+ * which are bound by HBM bandwidth: reads every byte of a packed [n, k]
+ * weight with the same loads, in the same order and launch shape as the
+ * weight-streaming decode kernel (one workgroup per 32-column slab, four
+ * waves splitting its K range), and does no arithmetic.  Its time is the
+ * practical ceiling against which a decode GEMM's time is judged.
+ *
+ *   w_packed  from nvfp4_pack_weights with the same n, k (16-byte aligned).
+ *   sink      device uint32, written only in the (practically impossible)
+ *             case that the XOR of all words equals 0x9E3779B9.
+ */
+int nvfp4_weight_stream_read(const void* w_packed, int64_t n, int64_t k, uint32_t* sink, nvfp4_stream_t stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* nvfp4_status_string(int status);

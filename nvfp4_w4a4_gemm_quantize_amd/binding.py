@@ -33,12 +33,15 @@ _SIGNATURES = {
     "nvfp4_pack_weights": (_int, [_c_p, _i64, _i64, _int, _c_p, _c_p, _int, _c_p, ctypes.c_size_t, _c_p]),
     "nvfp4_unpack_weights_linear": (_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "gemm_w4a4": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _int, _i64, _int, _c_p]),
+    "nvfp4_linear": (_int, [_c_p, _i64, _i64, _i64, _c_p, _int, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _int, _i64,
+                            _int, _c_p]),
     "gemm_w4a4_fused_segments": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i64, _i64, _int, _c_p, _c_p, _c_p,
                                         _c_p, _c_p, _c_p, _int, _i64, _c_p]),
     "gemm_w4a4_silu_mul_quantize": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p,
                                            _c_p, _c_p]),
     "gdn_recurrence": (_int, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _i64, _i64, _int, _int, _int,
                               _c_p, _c_p, _c_p, _int, _i64, _c_p]),
+    "nvfp4_weight_stream_read": (_int, [_c_p, _i64, _i64, _c_p, _c_p]),
     "nvfp4_status_string": (ctypes.c_char_p, [_int]),
     "nvfp4_last_hip_error": (_int, []),
 }
@@ -218,6 +221,42 @@ def gemm_w4a4(a_codes, a_scales, a_global, w_packed, w_global, n, k, out_dtype=t
     return out
 
 
+def nvfp4_linear(x, w_packed, w_global, n, out_dtype=torch.bfloat16, epilogue="none", out=None,
+                 a_global=None, dynamic=True, a_codes=None, a_scales=None):
+    """The W4A4 layer on a bf16 activation x [m, k]: quantise x (as nvfp4_quantize) and multiply.
+    Returns (out, a_codes, a_scales, a_global)."""
+    lib = load()
+    _dev(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise NVFP4Error("x must be 2-D with unit column stride")
+    m, k = x.shape
+    _dev(w_packed, torch.uint8, "w_packed")
+    _dev(w_global, torch.float32, "w_global")
+    if a_global is None:
+        if not dynamic:
+            raise NVFP4Error("a static quantisation needs a_global")
+        a_global = torch.empty(1, dtype=torch.float32, device=x.device)
+    _dev(a_global, torch.float32, "a_global")
+    if a_codes is None:
+        a_codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if a_scales is None:
+        a_scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
+    _dev(a_codes, torch.uint8, "a_codes")
+    _dev(a_scales, torch.uint8, "a_scales")
+    if a_codes.numel() != m * (k // 2) or a_scales.numel() != m * (k // 16) or not a_codes.is_contiguous() \
+            or not a_scales.is_contiguous():
+        raise NVFP4Error("a_codes/a_scales must be contiguous [m, k/2] and [m, k/16]")
+    if w_packed.numel() < nvfp4_packed_weight_bytes(n, k):
+        raise NVFP4Error("w_packed is smaller than the packed size of [%d, %d]" % (n, k))
+    epi = _EPI_NAMES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    out, od = _out(out, m, n // 2 if epi == EPI_SILU_MUL else n, out_dtype, x.device)
+    ld_x = x.stride(0) if m > 1 else k
+    rc = lib.nvfp4_linear(_ptr(x), m, k, ld_x, _ptr(a_global), 1 if dynamic else 0, _ptr(a_codes), _ptr(a_scales),
+                          _ptr(w_packed), _ptr(w_global), n, _ptr(out), od, _ld(out), epi, _stream())
+    _check(rc, "nvfp4_linear")
+    return out, a_codes, a_scales, a_global
+
+
 def gemm_w4a4_fused_segments(a_codes, a_scales, a_global, w_packed, n, k, seg_offsets, seg_w_global,
                              seg_epilogue=None, a_log=None, dt_bias=None, out_dtype=torch.bfloat16, out=None):
     """One GEMM over a fused weight; column segment s gets alpha_s = 1/(g_a g_w[s]) and its epilogue."""
@@ -286,6 +325,18 @@ def gemm_w4a4_silu_mul_quantize(a_codes, a_scales, a_global, w_packed, w_global,
                                          _ptr(h), _stream())
     _check(rc, "gemm_w4a4_silu_mul_quantize")
     return (h_codes, h_scales, h) if return_h else (h_codes, h_scales)
+
+
+def nvfp4_weight_stream_read(w_packed, n, k, sink=None):
+    """Read a packed weight exactly as the decode GEMM streams it, without arithmetic (roofline reference)."""
+    lib = load()
+    _dev(w_packed, torch.uint8, "w_packed")
+    if w_packed.numel() < nvfp4_packed_weight_bytes(n, k):
+        raise NVFP4Error("w_packed is smaller than the packed size of [%d, %d]" % (n, k))
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=w_packed.device)
+    _check(lib.nvfp4_weight_stream_read(_ptr(w_packed), n, k, _ptr(sink), _stream()), "nvfp4_weight_stream_read")
+    return sink
 
 
 def _ld2(t, name):

@@ -21,7 +21,7 @@ LIB = os.path.join(LIB_DIR, "libnvfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "gemm.hip", "recurrence.hip", "abi.cpp", "validate.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "decode.hip", "recurrence.hip", "abi.cpp", "validate.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I" + os.path.join(ROOT, "include")]
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -23,6 +23,22 @@ static SegmentTable make_table(int num, const int64_t* off) {
   return t;
 }
 
+// Epilogue of a single-module GEMM (one segment, no gate), optionally SiLU*mul.
+static EpilogueArgs plain_epilogue(const float* a_global, const float* w_global, int64_t n, bool silu, int out_dtype,
+                                   int64_t ld_out) {
+  EpilogueArgs epi{};
+  epi.segs.num = 1;
+  epi.segs.off[0] = 0;
+  epi.segs.off[1] = n;
+  epi.seg_epi[0] = NVFP4_SEG_NONE;
+  epi.seg_w_global = w_global;
+  epi.a_global = a_global;
+  epi.silu_mul = silu ? 1 : 0;
+  epi.out_bf16 = out_dtype == NVFP4_OUT_BF16;
+  epi.ld_out = ld_out;
+  return epi;
+}
+
 extern "C" {
 
 int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float* global_scale,
@@ -68,18 +84,32 @@ int gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gl
   if (rc) return rc;
   if (m == 0) return NVFP4_OK;
   if (!w_global) return NVFP4_EINVAL;
-  EpilogueArgs epi{};
-  epi.segs.num = 1;
-  epi.segs.off[0] = 0;
-  epi.segs.off[1] = n;
-  epi.seg_epi[0] = NVFP4_SEG_NONE;
-  epi.seg_w_global = w_global;
-  epi.a_global = a_global;
-  epi.silu_mul = silu ? 1 : 0;
-  epi.out_bf16 = out_dtype == NVFP4_OUT_BF16;
-  epi.ld_out = ld_out;
+  EpilogueArgs epi = plain_epilogue(a_global, w_global, n, silu, out_dtype, ld_out);
   return hip_status(launch_gemm(a_codes, a_scales, m, static_cast<const uint8_t*>(w_packed), n, k, out, epi,
                                 (hipStream_t)stream));
+}
+
+int nvfp4_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x, float* a_global, int dynamic_global,
+                 uint8_t* a_codes, uint8_t* a_scales, const void* w_packed, const float* w_global, int64_t n,
+                 void* out, int out_dtype, int64_t ld_out, int epilogue, nvfp4_stream_t stream) {
+  if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_SILU_MUL) return NVFP4_EINVAL;
+  const bool silu = epilogue == NVFP4_EPI_SILU_MUL;
+  if (silu && (n <= 0 || n % 64 != 0)) return NVFP4_ESHAPE;
+  int rc = validate_quantize(x, m, k, ld_x, a_global, a_codes, a_scales);
+  if (rc) return rc;
+  rc = validate_gemm_common(a_codes, a_scales, a_global, m, w_packed, n, k, out, out_dtype, ld_out, silu ? n / 2 : n);
+  if (rc) return rc;
+  if (m == 0) return NVFP4_OK;
+  if (!w_global) return NVFP4_EINVAL;
+  EpilogueArgs epi = plain_epilogue(a_global, w_global, n, silu, out_dtype, ld_out);
+  QuantSource qs{};
+  qs.x = x;
+  qs.ld_x = ld_x;
+  qs.g = a_global;
+  qs.dynamic = dynamic_global != 0;
+  qs.codes = a_codes;
+  qs.scales = a_scales;
+  return hip_status(launch_linear(qs, m, static_cast<const uint8_t*>(w_packed), n, k, out, epi, (hipStream_t)stream));
 }
 
 int gemm_w4a4_fused_segments(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t m,
@@ -168,6 +198,12 @@ int gdn_recurrence(const uint16_t* q, int64_t ld_q, const uint16_t* k, int64_t l
   a.o_bf16 = out_dtype == NVFP4_OUT_BF16;
   a.ld_o = ld_out;
   return hip_status(launch_gdn_recurrence(a, (hipStream_t)stream));
+}
+
+int nvfp4_weight_stream_read(const void* w_packed, int64_t n, int64_t k, uint32_t* sink, nvfp4_stream_t stream) {
+  int rc = validate_unpack(w_packed, n, k, sink, sink);
+  if (rc) return rc;
+  return hip_status(launch_weight_stream_read(static_cast<const uint8_t*>(w_packed), n, k, sink, (hipStream_t)stream));
 }
 
 const char* nvfp4_status_string(int status) {

@@ -16,125 +16,12 @@
 // lane's dword s: K positions 32h + 8s .. +7 -- the same set for A and W, so
 // the contraction is over every K exactly once.  The 16 accumulators of lane
 // l hold rows 8*(j/4) + 4h + (j%4) of column r.
+#include "epilogue.h"
 #include "kernels.h"
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
 
-// ----------------------------------------------------------- epilogue ----
-struct ColumnEpilogue {
-  float alpha;
-  int type;
-  float exp_alog;  // exp(A_log[h]) for the decay segment
-  float dt_bias;
-};
-
-// The column's segment by a scan over the segment table.  The table and the
-// segments' scales and gate types are read at wave-uniform addresses (scalar
-// loads, no dependent chain); each lane only selects.  Columns of the decay
-// segment also read their head's A_log and dt_bias.
-__device__ __forceinline__ ColumnEpilogue column_epilogue(const EpilogueArgs& e, int64_t col, float ga) {
-  float gw = e.seg_w_global[0];
-  int type = e.seg_epi[0];
-  int64_t first = 0;
-  for (int s = 1; s < e.segs.num; ++s) {
-    const int64_t o = e.segs.off[s];
-    const float g = e.seg_w_global[s];
-    const int t = e.seg_epi[s];
-    if (col >= o) {
-      gw = g;
-      type = t;
-      first = o;
-    }
-  }
-  ColumnEpilogue c;
-  c.alpha = 1.0f / (ga * gw);
-  c.type = type;
-  c.exp_alog = 0.0f;
-  c.dt_bias = 0.0f;
-  if (type == 2) {
-    const int64_t h = col - first;
-    c.exp_alog = expf(e.a_log[h]);
-    c.dt_bias = e.dt_bias[h];
-  }
-  return c;
-}
-
-// Per-column epilogue parameters of a workgroup's BN output columns
-// (col_base ...), written to LDS once per workgroup before its main loop so
-// the epilogue reads one LDS entry per column instead of searching the
-// segment table and dividing for every output.  Columns past n (never
-// stored) get no gate, so a padded tile does no gate arithmetic for them.
-template <int BN, int NT>
-__device__ __forceinline__ void fill_column_table(ColumnEpilogue* tab, const EpilogueArgs& e, int64_t col_base,
-                                                  int64_t n) {
-  const float ga = *e.a_global;
-  for (int c = (int)threadIdx.x; c < BN; c += NT) {
-    const int64_t col = col_base + c;
-    ColumnEpilogue ce = column_epilogue(e, col < n ? col : n - 1, ga);
-    if (col >= n) ce.type = 0;
-    tab[c] = ce;
-  }
-}
-
-constexpr float kLog2e = 1.44269504088896341f;
-constexpr float kLn2 = 0.693147180559945309f;
-
-// 1 / (1 + e^-y) on the hardware exp2 and reciprocal.
-__device__ __forceinline__ float sigmoid_f(float y) {
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * kLog2e));
-}
-
-// log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  log1p(e) is taken as
-// log(u) * e / (u - 1) with u = 1 + e rounded (u - 1 is exact), which keeps
-// the relative accuracy of small e; u == 1 gives e itself.
-__device__ __forceinline__ float softplus_f(float x) {
-  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-  const float u = 1.0f + e;
-  const float l = u == 1.0f ? e : __builtin_amdgcn_logf(u) * kLn2 * e * __builtin_amdgcn_rcpf(u - 1.0f);
-  return fmaxf(x, 0.0f) + l;
-}
-
-__device__ __forceinline__ float apply_epilogue(const ColumnEpilogue& c, float acc) {
-  float y = acc * c.alpha;
-  if (c.type == 1) {
-    y = sigmoid_f(y);
-  } else if (c.type == 2) {
-    y = -c.exp_alog * softplus_f(y + c.dt_bias);
-  }
-  return y;
-}
-
-// silu(g)*u = g*u / (1 + e^-g), with e^-g = 2^(-g*log2 e) on the hardware exp2
-// and the division as the hardware reciprocal (each within about an ulp of
-// fp32, far below the bf16 rounding of the result; e^-g = inf gives 0).
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
-  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-// The epilogue's LDS staging region belongs to one wave, and a wave's LDS
-// instructions execute in issue order, so only the compiler has to keep the
-// region's writes and reads in program order: no workgroup barrier.
-__device__ __forceinline__ void wave_lds_order() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void store_out(void* out, bool bf16, int64_t idx, float v) {
-  if (bf16) reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(v);
-  else reinterpret_cast<float*>(out)[idx] = v;
-}
-
-// ------------------------------------------------------ shared helpers ----
-// Load a 16-byte chunk if `ok`, zeros otherwise.
-__device__ __forceinline__ uint4 ld16(const uint8_t* p, bool ok) {
-  return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
-}
-
-// Scale pair (blocks 2h, 2h+1 of a 64-wide K tile) -> scale byte for sub-step s.
-__device__ __forceinline__ uint32_t scale_byte(uint32_t pair, int s) { return (pair >> (8 * (s >> 1))) & 0xFFu; }
 
 // ------------------------------------------------------ tile epilogue ----
 // Epilogue of a workgroup tile: each 32x32 accumulator fragment of a wave goes
@@ -876,583 +763,6 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
                                       SILU ? o0 : (int64_t)bx * BN, m, n, out, epi);
 }
 
-// ------------------------------------------------------- decode kernel ----
-// m <= 64: weight streaming.  One workgroup per 32-column weight slab (two
-// slabs -- gate and up -- for SILU); its waves split K evenly, each
-// streaming its part of the slab straight from HBM into registers with one
-// 16-byte load per lane per 64-wide K tile (the packed layout is already in
-// MFMA lane order).  Loads run up to eight tiles ahead of the MFMAs.
-// ALDS (small m*k): the workgroup first dequantises A once into LDS as f16 in
-// MFMA operand order (rows < m only; lanes of absent rows read a zero slot),
-// so the loop spends VALU only on the weights.  Otherwise A is dequantised
-// per tile in registers.  GA (k % 256 == 0, 16-byte aligned A scales): A is
-// fetched four K tiles at a time, eight lanes per 128-byte row segment, and
-// each wave re-orders its group through a private LDS area into MFMA lane
-// order -- a per-tile fetch in lane order would touch one cache line per row
-// per instruction, and at 32 or 64 rows those line lookups, not the bytes,
-// limit the kernel.  The waves' partial accumulators are summed in LDS in a
-// fixed order.
-constexpr int kDecodeALdsBytes = 48 * 1024;
-#ifndef NVFP4_DECODE_GROUP_A
-#define NVFP4_DECODE_GROUP_A 6
-#endif
-// Tiles per load group with A staged in LDS (two groups are in flight; six is
-// the most that fits three waves per SIMD without spilling).
-constexpr int kDecodeGroupA = NVFP4_DECODE_GROUP_A;
-
-// Sized so that three 4-wave workgroups fit on a CU (<= 168 VGPRs per wave,
-// A staging in dynamic LDS of exactly (m+1)*k*2 bytes): the 544 workgroups of
-// a 17408-column projection are then all resident at once instead of the
-// last few running as a second round.
-constexpr int kDecodeGroupRow = 144;          // LDS bytes per A row of a group (128 + 16: conflict-free reads)
-constexpr int kDecodeGroupFrag = 32 * kDecodeGroupRow;
-
-template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U, bool GA>
-__global__ void __launch_bounds__(DW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
-gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
-                   const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
-                   EpilogueArgs epi) {
-  constexpr int NS = SILU ? 2 : 1;                 // weight slabs per workgroup
-  constexpr int NACC = MFD * NS;
-  static_assert(!GA || (!ALDS && U == 4), "grouped A fetch: four tiles per load group");
-  __shared__ float s_red[DW - 1][NACC][16][64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_ag[GA ? DW * MFD * kDecodeGroupFrag : 16];
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_a[];    // ALDS: (m+1)*k*2 bytes
-
-  const int t = threadIdx.x;
-  const int lane = t & 63, r = lane & 31, h = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t KT = (k + kTileK - 1) / kTileK;
-  const int64_t KS = super_count(k);
-  const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
-  int64_t slab[NS];
-  slab[0] = blockIdx.x;
-  if (SILU) slab[NS - 1] = blockIdx.x + (n / 2) / kTileN;
-  // GA: wave ranges in whole groups of four tiles (KT % 4 == 0 there)
-  const int64_t kt0 = GA ? (KT / 4) * wave / DW * 4 : KT * wave / DW;
-  const int64_t kt1 = GA ? (KT / 4) * (wave + 1) / DW * 4 : KT * (wave + 1) / DW;
-
-  // Independent accumulators per K sub-step break the MFMA dependency chain
-  // (a single 32x32 output tile would otherwise serialise every MFMA).
-  constexpr int NSUB = 2;
-  floatx16 part[MFD][NS][NSUB];
-#pragma unroll
-  for (int i = 0; i < MFD; ++i)
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-#pragma unroll
-      for (int q = 0; q < NSUB; ++q)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) part[i][j][q][e] = 0.0f;
-
-  // Per-lane constant offsets; per-tile bases are wave-uniform (scalar).
-  const uint32_t w_lane = lane * 16, ws_lane = r * 8 + 2 * h;
-  // A in LDS (ALDS): 16-byte chunk (kt, s, hh, row) at ((kt*4 + s)*2 + hh)*(m+1) + row,
-  // row m of every group is zero; lanes of rows >= m read it.
-  const int64_t a_rows = m + 1;
-  const uint32_t a_lane = (uint32_t)((h * a_rows + (r < m ? r : m)) * 16);
-
-  constexpr bool ATILE = !ALDS && !GA;             // A fetched per tile in lane order
-  struct Tile { uint4 a[ATILE ? MFD : 1]; uint32_t as[ATILE ? MFD : 1]; uint4 b[NS]; uint32_t bs[NS]; };
-  // Loads are unconditional (no branches, so the compiler can count them and
-  // wait only for the group about to be multiplied); tiles past the wave's
-  // range are clamped to its last tile and never multiplied.
-  auto load = [&](int64_t kt, Tile& T) __attribute__((always_inline)) {
-    kt = kt < kt1 ? kt : kt1 - 1;
-    if constexpr (ATILE) {
-#pragma unroll
-      for (int i = 0; i < MFD; ++i) {
-        const int64_t row = i * 32 + r;
-        const bool ok = row < m && (kt * 64 + h * 32) < k;
-        T.a[i] = ld16(a_codes + row * a_row_bytes + kt * 32 + h * 16, ok);
-        T.as[i] = ok ? *reinterpret_cast<const uint16_t*>(a_scales + row * a_row_scales + kt * 4 + 2 * h) : 0u;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {                                 // tile bases are wave-uniform
-      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile_code_off(slab[j], kt, KS) + w_lane);
-      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_packed + tile_scale_off(slab[j], kt, KS, 0) + ws_lane);
-    }
-  };
-  // A of one tile for the non-ALDS paths: codes (16 bytes: K half h of row
-  // i*32 + r) and the scale pair of those two blocks.
-  struct ATileRegs { uint4 a[MFD]; uint32_t as[MFD]; };
-  auto compute = [&](int64_t kt, const Tile& T, const ATileRegs& A) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      half8_t av[MFD], bv[NS];
-      if constexpr (ALDS) {
-        const uint32_t grp = (uint32_t)((kt * 4 + s) * 2 * a_rows * 16);   // wave-uniform
-        av[0] = *reinterpret_cast<const half8_t*>(s_a + grp + a_lane);
-      } else {
-#pragma unroll
-        for (int i = 0; i < MFD; ++i) {
-          const uint32_t cw = s == 0 ? A.a[i].x : s == 1 ? A.a[i].y : s == 2 ? A.a[i].z : A.a[i].w;
-          av[i] = dequant8(cw, scale_pair_f16(scale_byte(A.as[i], s)));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const uint32_t cw = s == 0 ? T.b[j].x : s == 1 ? T.b[j].y : s == 2 ? T.b[j].z : T.b[j].w;
-        bv[j] = dequant8(cw, scale_pair_f16(scale_byte(T.bs[j], s)));
-      }
-#pragma unroll
-      for (int i = 0; i < MFD; ++i)
-#pragma unroll
-        for (int j = 0; j < NS; ++j) part[i][j][s % NSUB] = mfma32x32x16(av[i], bv[j], part[i][j][s % NSUB]);
-    }
-  };
-  // GA: one group's A -- codes of rows i*32 + 8j + lane/8, 16-byte segment
-  // lane%8 of the group's 128 bytes per row, and each lane's row i*32 + r's
-  // scales for the group's four tiles (16 bytes).
-  struct AGroup { uint4 c[GA ? MFD : 1][GA ? 4 : 1]; uint4 s[GA ? MFD : 1]; };
-  uint8_t* const ag_base = s_ag + (GA ? wave * MFD * kDecodeGroupFrag : 0);
-  auto load_agroup = [&](int64_t g0, AGroup& G) __attribute__((always_inline)) {
-    if constexpr (GA) {
-      g0 = g0 < kt1 - 4 ? g0 : kt1 - 4;              // groups past the wave's range: never multiplied
-#pragma unroll
-      for (int i = 0; i < MFD; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t row = i * 32 + 8 * j + (lane >> 3);
-          G.c[i][j] = ld16(a_codes + row * a_row_bytes + g0 * 32 + (lane & 7) * 16, row < m);
-        }
-        const int64_t row = i * 32 + r;
-        G.s[i] = ld16(a_scales + row * a_row_scales + g0 * 4, row < m);
-      }
-    }
-  };
-  auto load_group = [&](int64_t g0, Tile (&T)[U], AGroup& G) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) load(g0 + u, T[u]);
-    load_agroup(g0, G);
-  };
-  auto compute_group = [&](int64_t g0, const Tile (&T)[U], const AGroup& G) __attribute__((always_inline)) {
-    if constexpr (GA) {
-      // this wave's group through its LDS area into lane order (the previous
-      // group's reads were issued before these writes)
-#pragma unroll
-      for (int i = 0; i < MFD; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint4*>(ag_base + i * kDecodeGroupFrag + (8 * j + (lane >> 3)) * kDecodeGroupRow +
-                                    (lane & 7) * 16) = G.c[i][j];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (g0 + u < kt1) {
-        ATileRegs A;
-        if constexpr (GA) {
-#pragma unroll
-          for (int i = 0; i < MFD; ++i) {
-            A.a[i] = *reinterpret_cast<const uint4*>(ag_base + i * kDecodeGroupFrag + r * kDecodeGroupRow +
-                                                     (2 * u + h) * 16);
-            const uint32_t w = u == 0 ? G.s[i].x : u == 1 ? G.s[i].y : u == 2 ? G.s[i].z : G.s[i].w;
-            A.as[i] = (w >> (16 * h)) & 0xFFFFu;
-          }
-        } else if constexpr (ATILE) {
-#pragma unroll
-          for (int i = 0; i < MFD; ++i) {
-            A.a[i] = T[u].a[i];
-            A.as[i] = T[u].as[i];
-          }
-        }
-        compute(g0 + u, T[u], A);
-      }
-    }
-  };
-
-  // The first weight group is requested before A is staged, so its latency
-  // overlaps the staging.
-  Tile g_a[U], g_b[U];
-  AGroup ag_a, ag_b;
-  if (kt0 < kt1) load_group(kt0, g_a, ag_a);
-  // Stage A into LDS once per workgroup (ALDS): dequantised f16 chunks in MFMA
-  // operand order plus one zero row per (kt, s, hh) group.
-  if constexpr (ALDS) {
-    const int64_t items = a_rows * KT * 2;         // (row, kt, hh): 32 values each
-    for (int64_t it = t; it < items; it += DW * 64) {
-      const int64_t row = it / (KT * 2), rem = it % (KT * 2), kt = rem >> 1, hh = rem & 1;
-      uint4 c = make_uint4(0u, 0u, 0u, 0u);
-      uint32_t sp = 0;
-      if (row < m && kt * 64 + hh * 32 < k) {
-        c = *reinterpret_cast<const uint4*>(a_codes + row * a_row_bytes + kt * 32 + hh * 16);
-        sp = *reinterpret_cast<const uint16_t*>(a_scales + row * a_row_scales + kt * 4 + 2 * hh);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t cw = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
-        *reinterpret_cast<half8_t*>(s_a + (((kt * 4 + s) * 2 + hh) * a_rows + row) * 16) =
-            dequant8(cw, scale_pair_f16(scale_byte(sp, s)));
-      }
-    }
-    __syncthreads();
-  }
-
-  if (kt0 < kt1) {
-    for (int64_t g = kt0; g < kt1; g += 2 * U) {
-      load_group(g + U, g_b, ag_b);
-      compute_group(g, g_a, ag_a);
-      load_group(g + 2 * U, g_a, ag_a);
-      compute_group(g + U, g_b, ag_b);
-    }
-  }
-
-  floatx16 acc[MFD][NS];
-#pragma unroll
-  for (int i = 0; i < MFD; ++i)
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      acc[i][j] = part[i][j][0];
-#pragma unroll
-      for (int q = 1; q < NSUB; ++q) acc[i][j] += part[i][j][q];
-    }
-
-  if (wave > 0) {
-#pragma unroll
-    for (int i = 0; i < MFD; ++i)
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s_red[wave - 1][i * NS + j][e][lane] = acc[i][j][e];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < DW - 1; ++w)
-#pragma unroll
-    for (int i = 0; i < MFD; ++i)
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] += s_red[w][i * NS + j][e][lane];
-
-  const float ga = *epi.a_global;
-  const bool bf16 = epi.out_bf16 != 0;
-  if (SILU) {
-    const float alpha = 1.0f / (ga * epi.seg_w_global[0]);
-    const int64_t col = slab[0] * 32 + r;
-    if (col >= n / 2) return;
-#pragma unroll
-    for (int i = 0; i < MFD; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (row < m) store_out(out, bf16, row * epi.ld_out + col,
-                               silu_mul(acc[i][0][e] * alpha, acc[i][NS - 1][e] * alpha));
-      }
-  } else {
-    const int64_t col = slab[0] * 32 + r;
-    if (col >= n) return;
-    const ColumnEpilogue ce = column_epilogue(epi, col, ga);
-#pragma unroll
-    for (int i = 0; i < MFD; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (row < m) store_out(out, bf16, row * epi.ld_out + col, apply_epilogue(ce, acc[i][0][e]));
-      }
-  }
-}
-
-// ------------------------------------------------ decode kernel, FP4 MFMA ----
-// m <= 4: weight streaming on gfx950's block-scaled FP4 MFMA, applied to the
-// raw E2M1 codes (no dequantisation).  The packed weight tile is already the
-// B operand of v_mfma_scale_f32_32x32x64_f8f6f4 (lane r + 32h: column r, K
-// 32h..32h+31).  The A operand puts each 16-element block of each A row in a
-// row of its own -- MFMA row 4*mm + q holds row mm's block q of the tile and
-// zeros elsewhere -- so with unit E8M0 scales the 32x32 result holds the
-// per-block partial sums sum_{k in block q} a[mm][k] * w[n][k], exactly (the
-// products are multiples of 1/4 and a block sum stays far below 2^24).  Each
-// lane then applies the NVFP4 block scales in FP32:
-//   y[mm][n] += sum_q s_a[mm][q] * s_w[n][q] * C[4*mm + q][n].
-// Lane (r, h) holds rows mm = h, 2+h, ... of column r, so no cross-lane
-// reduction is needed; the K split across the workgroup's waves is summed in
-// LDS in a fixed order.  A is staged once per workgroup into LDS: one 16-byte
-// operand record per (tile, block, row) plus one zero record per tile (for
-// lanes whose MFMA row is empty), and the A block scales as FP32.
-typedef int v8i_t __attribute__((ext_vector_type(8)));
-
-template <int MR>
-struct Fp4DecodeLds {
-  static constexpr int RECS = 4 * MR + 1;           // records per K tile (last: zeros)
-  __host__ __device__ static int64_t rec_bytes(int64_t kt_count) { return kt_count * RECS * 16; }
-  __host__ __device__ static int64_t scale_bytes(int64_t kt_count) { return (int64_t)MR * kt_count * 4 * 4; }
-};
-
-template <int MR, bool SILU, int DW, int SU>
-__global__ void __launch_bounds__(DW * 64) __attribute__((amdgpu_waves_per_eu(3)))
-gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
-                       const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
-                       EpilogueArgs epi) {
-  constexpr int NS = SILU ? 2 : 1;               // weight slabs per workgroup (gate, up)
-  constexpr int MH = MR / 2;                     // A rows per lane: h, 2+h, ...
-  using L = Fp4DecodeLds<MR>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-
-  const int t = threadIdx.x;
-  const int lane = t & 63, r = lane & 31, h = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t KS = super_count(k), KTP = KS * kSuperTiles;   // tiles incl. zero padding
-  const int64_t a_row_bytes = k / 2, a_row_scales = k / 16;
-  int64_t slab[NS];
-  slab[0] = blockIdx.x;
-  if (SILU) slab[NS - 1] = blockIdx.x + (n / 2) / kTileN;
-  // The waves split the slab's super-tiles (padding tiles hold zeros).
-  const int64_t ks0 = KS * wave / DW, ks1 = KS * (wave + 1) / DW;
-  const int64_t rec_total = L::rec_bytes(KTP) / 16;
-  float* s_sa = reinterpret_cast<float*>(smem + L::rec_bytes(KTP));
-
-  // One super-tile of each slab: four tiles of codes and, per lane, row r's
-  // scales for tiles 2h and 2h+1 (the other pair comes from lane r + 32(1-h)).
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-  struct Super { uint4 b[NS][kSuperTiles]; uint2 bs[NS]; };
-  // Streaming loads (non-temporal: the weights are read once), unconditional
-  // and clamped to the wave's range so the compiler can count them.
-  auto load = [&](int64_t ks, Super& S) __attribute__((always_inline)) {
-    ks = ks < ks1 ? ks : ks1 - 1;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const uint8_t* sp = w_packed + (slab[j] * KS + ks) * kSuperBytes;   // wave-uniform
-#pragma unroll
-      for (int tt = 0; tt < kSuperTiles; ++tt) {
-        const u32x4_t cv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(sp + tt * kTileCodeBytes + lane * 16));
-        S.b[j][tt] = make_uint4(cv[0], cv[1], cv[2], cv[3]);
-      }
-      const u32x2_t sv = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sp + kSuperScaleOff + lane * 8));
-      S.bs[j] = make_uint2(sv[0], sv[1]);
-    }
-  };
-  Super g_a[SU], g_b[SU];
-  auto load_group = [&](int64_t g0, Super (&G)[SU]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < SU; ++u) load(g0 + u, G[u]);
-  };
-
-  // Stage A: operand records (one per (tile, block, row), plus a zero record
-  // per tile) and FP32 block scales.  When A is small (the usual decode case)
-  // a fixed, unrolled set of unconditional staging loads (invalid items read
-  // offset 0, which always exists, and are zeroed afterwards) is issued before
-  // the weight loads, so waiting for it does not wait for the weight stream.
-  constexpr int SPT = 4;
-  const uint32_t kt4 = (uint32_t)KTP * 4u, k32 = (uint32_t)k, m32 = (uint32_t)m;
-  const uint32_t nrec = (uint32_t)rec_total, nsc = (uint32_t)MR * kt4;
-  const bool fast_stage = nrec <= (uint32_t)(SPT * DW * 64) && nsc <= (uint32_t)(SPT * DW * 64);
-  auto rec_of = [&](uint32_t idx, bool& ok, bool& odd) __attribute__((always_inline)) -> uint32_t {
-    const uint32_t kt = idx / L::RECS, rr = idx % L::RECS;
-    const uint32_t q = rr / MR, mm = rr % MR;
-    ok = idx < nrec && rr < 4 * MR && mm < m32 && kt * kTileK + q * 16 < k32;
-    odd = (q & 1) != 0;
-    return ok ? mm * (uint32_t)a_row_bytes + kt * 32 + q * 8 : 0u;
-  };
-  auto scale_of = [&](uint32_t idx, bool& ok) __attribute__((always_inline)) -> uint32_t {
-    const uint32_t mm = idx / kt4, b = idx - mm * kt4;
-    ok = idx < nsc && mm < m32 && b * 16 < k32;
-    return ok ? mm * (uint32_t)a_row_scales + b : 0u;
-  };
-  auto record = [&](uint2 c, bool ok, bool odd) __attribute__((always_inline)) -> uint4 {
-    if (!ok) c = make_uint2(0u, 0u);
-    return odd ? make_uint4(0u, 0u, c.x, c.y) : make_uint4(c.x, c.y, 0u, 0u);
-  };
-  if (fast_stage) {
-    uint2 rc[SPT];
-    uint32_t sc[SPT];
-    bool rok[SPT], sok[SPT], rodd[SPT];
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const uint32_t idx = (uint32_t)t + (uint32_t)(i * DW * 64);
-      rc[i] = *reinterpret_cast<const uint2*>(a_codes + rec_of(idx, rok[i], rodd[i]));
-      sc[i] = a_scales[scale_of(idx, sok[i])];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (ks0 < ks1) { load_group(ks0, g_a); load_group(ks0 + SU, g_b); }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const uint32_t idx = (uint32_t)t + (uint32_t)(i * DW * 64);
-      if (idx < nrec) *reinterpret_cast<uint4*>(smem + idx * 16) = record(rc[i], rok[i], rodd[i]);
-      if (idx < nsc) s_sa[idx] = sok[i] ? e4m3_decode(sc[i]) : 0.0f;
-    }
-  } else {
-    if (ks0 < ks1) { load_group(ks0, g_a); load_group(ks0 + SU, g_b); }
-    for (uint32_t idx = t; idx < nrec; idx += DW * 64) {
-      bool ok, odd;
-      const uint32_t off = rec_of(idx, ok, odd);
-      uint2 c = make_uint2(0u, 0u);
-      if (ok) c = *reinterpret_cast<const uint2*>(a_codes + off);
-      *reinterpret_cast<uint4*>(smem + idx * 16) = record(c, ok, odd);
-    }
-    for (uint32_t idx = t; idx < nsc; idx += DW * 64) {
-      bool ok;
-      const uint32_t off = scale_of(idx, ok);
-      s_sa[idx] = ok ? e4m3_decode(a_scales[off]) : 0.0f;
-    }
-  }
-  __syncthreads();
-
-  // This lane's A operand record within a tile: MFMA row r = 4*amm + aq.
-  const int amm = r >> 2, aq = r & 3;
-  const bool a_on = amm < MR && h == (aq >> 1);
-  const uint32_t a_lane = a_on ? (uint32_t)((aq * MR + amm) * 16) : (uint32_t)(4 * MR * 16);
-
-  // Partial sums per (slab, row, block slot): the four block slots of a tile
-  // feed four independent chains, so a chain adds one term per tile (K/64
-  // terms in all, split further over the waves) and its FP32 rounding stays
-  // far below the 1e-5 * sum|a*w| acceptance bound at any K that fits LDS.
-  constexpr int QC = 4;
-  float y4[NS][MH][QC];
-#pragma unroll
-  for (int j = 0; j < NS; ++j)
-#pragma unroll
-    for (int i = 0; i < MH; ++i)
-#pragma unroll
-      for (int q = 0; q < QC; ++q) y4[j][i][q] = 0.0f;
-
-  // One tile: its MFMA results and the FP32 scale products s_a * s_w.
-  struct Prod { floatx16 c[NS]; float p[NS][MH][4]; };
-  auto tile_mfma = [&](int64_t kt, const uint4 (&wb)[NS], const uint32_t (&ws)[NS], Prod& P)
-      __attribute__((always_inline)) {
-    const uint4 a4 = *reinterpret_cast<const uint4*>(smem + kt * (L::RECS * 16) + a_lane);
-    const v8i_t av = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
-    float4 sa[MH];
-#pragma unroll
-    for (int i = 0; i < MH; ++i) sa[i] = *reinterpret_cast<const float4*>(s_sa + ((2 * i + h) * KTP + kt) * 4);
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const v8i_t bv = {(int)wb[j].x, (int)wb[j].y, (int)wb[j].z, (int)wb[j].w, 0, 0, 0, 0};
-      const floatx16 zero = {};
-      P.c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, zero, 4, 4, 0, 127, 0, 127);
-      const float sw0 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 0);
-      const float sw1 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 1);
-      const float sw2 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 2);
-      const float sw3 = __builtin_amdgcn_cvt_f32_fp8((int)ws[j], 3);
-#pragma unroll
-      for (int i = 0; i < MH; ++i) {
-        P.p[j][i][0] = sa[i].x * sw0;
-        P.p[j][i][1] = sa[i].y * sw1;
-        P.p[j][i][2] = sa[i].z * sw2;
-        P.p[j][i][3] = sa[i].w * sw3;
-      }
-    }
-  };
-  auto tile_accumulate = [&](const Prod& P) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-#pragma unroll
-      for (int i = 0; i < MH; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y4[j][i][q % QC] += P.p[j][i][q] * P.c[j][4 * i + q];
-  };
-  // One super-tile, branch-free: row r's scales for all four tiles (own pair
-  // plus the other half's), then tile u+1's MFMA issued before tile u's
-  // results are scaled and accumulated (with several rows or slabs per lane
-  // two tiles' state does not fit the register budget; those run in order).
-  auto compute_super = [&](int64_t ks, const Super& S) __attribute__((always_inline)) {
-    uint32_t ws[kSuperTiles][NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const uint32_t o0 = (uint32_t)__shfl_xor((int)S.bs[j].x, 32, 64);
-      const uint32_t o1 = (uint32_t)__shfl_xor((int)S.bs[j].y, 32, 64);
-      ws[0][j] = h == 0 ? S.bs[j].x : o0;
-      ws[1][j] = h == 0 ? S.bs[j].y : o1;
-      ws[2][j] = h == 0 ? o0 : S.bs[j].x;
-      ws[3][j] = h == 0 ? o1 : S.bs[j].y;
-    }
-    auto wb = [&](int tt, uint4 (&o)[NS]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int j = 0; j < NS; ++j) o[j] = S.b[j][tt];
-    };
-    const int64_t kt = ks * kSuperTiles;
-    if constexpr (NS * MH <= 2) {
-      Prod P[2];
-      uint4 b0[NS];
-      wb(0, b0);
-      tile_mfma(kt, b0, ws[0], P[0]);
-#pragma unroll
-      for (int u = 1; u < kSuperTiles; ++u) {
-        uint4 bu[NS];
-        wb(u, bu);
-        tile_mfma(kt + u, bu, ws[u], P[u & 1]);
-        tile_accumulate(P[(u - 1) & 1]);
-      }
-      tile_accumulate(P[(kSuperTiles - 1) & 1]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < kSuperTiles; ++u) {
-        uint4 bu[NS];
-        wb(u, bu);
-        Prod P1;
-        tile_mfma(kt + u, bu, ws[u], P1);
-        tile_accumulate(P1);
-      }
-    }
-  };
-  auto compute_group = [&](int64_t g0, const Super (&G)[SU]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < SU; ++u)
-      if (g0 + u < ks1) compute_super(g0 + u, G[u]);
-  };
-  // Two groups of SU super-tiles in flight; each group is refilled after use.
-  if (ks0 < ks1) {
-    for (int64_t g = ks0; g < ks1; g += 2 * SU) {
-      compute_group(g, g_a);
-      if (g + 2 * SU < ks1) load_group(g + 2 * SU, g_a);
-      if (g + SU < ks1) compute_group(g + SU, g_b);
-      if (g + 3 * SU < ks1) load_group(g + 3 * SU, g_b);
-    }
-  }
-  float y[NS][MH];
-#pragma unroll
-  for (int j = 0; j < NS; ++j)
-#pragma unroll
-    for (int i = 0; i < MH; ++i) {
-      float v = y4[j][i][0];
-#pragma unroll
-      for (int q = 1; q < QC; ++q) v += y4[j][i][q];
-      y[j][i] = v;
-    }
-
-  // Sum the waves' partial results in LDS (reusing the A staging area).
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
-  if (wave > 0) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-#pragma unroll
-      for (int i = 0; i < MH; ++i) red[(((wave - 1) * NS + j) * MH + i) * 64 + lane] = y[j][i];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < DW - 1; ++w)
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-#pragma unroll
-      for (int i = 0; i < MH; ++i) y[j][i] += red[((w * NS + j) * MH + i) * 64 + lane];
-
-  const float ga = *epi.a_global;
-  const bool bf16 = epi.out_bf16 != 0;
-  const int64_t col = slab[0] * kTileN + r;
-  if (SILU) {
-    if (col >= n / 2) return;
-    const float alpha = 1.0f / (ga * epi.seg_w_global[0]);
-#pragma unroll
-    for (int i = 0; i < MH; ++i) {
-      const int64_t row = 2 * i + h;
-      if (row < m) store_out(out, bf16, row * epi.ld_out + col, silu_mul(y[0][i] * alpha, y[NS - 1][i] * alpha));
-    }
-  } else {
-    if (col >= n) return;
-    const ColumnEpilogue ce = column_epilogue(epi, col, ga);
-#pragma unroll
-    for (int i = 0; i < MH; ++i) {
-      const int64_t row = 2 * i + h;
-      if (row < m) store_out(out, bf16, row * epi.ld_out + col, apply_epilogue(ce, y[0][i]));
-    }
-  }
-}
-
 // ------------------------------------------------------------ launcher ----
 // Prefill tile: MF, NF (32x32 fragments per wave along M, N), WM, WN (waves), stages.
 #ifndef NVFP4_PREFILL_TILE
@@ -1540,73 +850,6 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
 // Decode launch shapes: every workgroup of a large projection must be resident
 // at once (544 of them for N = 17408), so the number of waves per workgroup
 // (the K split) and the register budget (waves per SIMD) are chosen together.
-template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U>
-static void launch_decode_kernel(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
-                                 int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
-  const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
-  const unsigned lds = ALDS ? (unsigned)((m + 1) * ((k + kTileK - 1) / kTileK) * kTileK * 2) : 0u;
-  // grouped A fetch: whole 4-tile groups per row (k % 256 == 0) and 16-byte scale loads
-  const bool ga = !ALDS && U == 4 && k % 256 == 0 && (reinterpret_cast<uintptr_t>(as) & 15u) == 0;
-  if constexpr (!ALDS && U == 4) {
-    if (ga) {
-      hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, true>), dim3((unsigned)slabs),
-                         dim3(DW * 64), lds, st, ac, as, m, w, n, k, out, epi);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, false>), dim3((unsigned)slabs), dim3(DW * 64),
-                     lds, st, ac, as, m, w, n, k, out, epi);
-}
-
-template <int MFD, bool SILU>
-static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
-                          int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
-  if constexpr (MFD == 1 && !SILU) {
-    if ((m + 1) * k * 2 <= kDecodeALdsBytes)
-      launch_decode_kernel<1, false, true, 4, 3, kDecodeGroupA>(ac, as, m, w, n, k, out, epi, st);
-    else
-      launch_decode_kernel<1, false, false, 4, 3, 4>(ac, as, m, w, n, k, out, epi, st);
-  } else if constexpr (MFD == 2 && SILU) {
-    launch_decode_kernel<2, true, false, 2, 1, 4>(ac, as, m, w, n, k, out, epi, st);
-  } else {
-    launch_decode_kernel<MFD, SILU, false, 2, 2, 4>(ac, as, m, w, n, k, out, epi, st);
-  }
-}
-
-// FP4-MFMA decode: LDS for the A records and scales (reused for the K-split
-// reduction); too large a K falls back to the f16 decode kernel.
-#ifndef NVFP4_DECODE_FP4_SU
-#define NVFP4_DECODE_FP4_SU 1
-#endif
-constexpr int kDecodeFp4Waves = 4;
-constexpr int64_t kDecodeFp4MaxLds = 56 * 1024;
-
-template <int MR, bool SILU>
-static bool launch_decode_fp4(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
-                              int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
-  using L = Fp4DecodeLds<MR>;
-  constexpr int DW = kDecodeFp4Waves;
-  const int64_t ktp = super_count(k) * kSuperTiles;
-  const int64_t red = (int64_t)(DW - 1) * (SILU ? 2 : 1) * (MR / 2) * 64 * 4;
-  int64_t lds = L::rec_bytes(ktp) + L::scale_bytes(ktp);
-  if (lds < red) lds = red;
-  if (lds > kDecodeFp4MaxLds) return false;
-  const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
-  hipLaunchKernelGGL((gemm_decode_fp4_kernel<MR, SILU, DW, NVFP4_DECODE_FP4_SU>), dim3((unsigned)slabs),
-                     dim3(DW * 64), (unsigned)lds, st, ac, as, m, w, n, k, out, epi);
-  return true;
-}
-
-// The FP4 path covers plain (non-SILU) GEMMs with m <= 4: wider tiles of rows
-// or a second (gate/up) slab exceed its register budget, and those shapes run
-// no faster than the f16 decode kernel.
-static bool try_decode_fp4(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
-                           int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
-  if (epi.silu_mul) return false;
-  if (m <= 2) return launch_decode_fp4<2, false>(ac, as, m, w, n, k, out, epi, st);
-  if (m <= 4) return launch_decode_fp4<4, false>(ac, as, m, w, n, k, out, epi, st);
-  return false;
-}
 
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                              int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
@@ -1614,23 +857,18 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, in
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
-                       int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
-  if (m <= 4 && try_decode_fp4(a_codes, a_scales, m, w_packed, n, k, out, epi, st)) return hipGetLastError();
-  // The f16 decode kernel moves A in 16-byte chunks (32 elements): K % 32 == 16
-  // runs the register-staged tile kernel, which reads A per 16-element block.
-  if (m <= 64 && k % 32 == 0) {
-    if (m <= 32) {
-      if (epi.silu_mul) launch_decode<1, true>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
-      else launch_decode<1, false>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
-    } else {
-      if (epi.silu_mul) launch_decode<2, true>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
-      else launch_decode<2, false>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
-    }
-  } else {
-    launch_prefill<NVFP4_PREFILL_TILE>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
-  }
-  return hipGetLastError();
+hipError_t launch_linear(const QuantSource& qs, int64_t m, const uint8_t* w_packed, int64_t n, int64_t k,
+                         void* out, const EpilogueArgs& epi, hipStream_t st) {
+  if (launch_gemm_decode_quantize(qs, m, w_packed, n, k, out, epi, st)) return hipGetLastError();
+  const hipError_t e = launch_quantize(qs.x, m, k, qs.ld_x, qs.g, qs.dynamic != 0, qs.codes, qs.scales, st);
+  if (e != hipSuccess) return e;
+  return launch_gemm(qs.codes, qs.scales, m, w_packed, n, k, out, epi, st);
 }
 
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
+                       int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+  if (!launch_gemm_decode(a_codes, a_scales, m, w_packed, n, k, out, epi, st))
+    launch_prefill<NVFP4_PREFILL_TILE>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
+  return hipGetLastError();
+}
 }  // namespace nvfp4

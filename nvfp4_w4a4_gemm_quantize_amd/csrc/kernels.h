@@ -71,6 +71,35 @@ struct GdnArgs {
 };
 hipError_t launch_gdn_recurrence(const GdnArgs& a, hipStream_t st);
 
+// Activation quantisation fused into a decode GEMM: the bf16 activation, its
+// global scale (written when dynamic, else read) and where the quantised
+// activation (codes [m, k/2], scales [m, k/16]) is written.
+struct QuantSource {
+  const uint16_t* x;
+  int64_t ld_x;
+  float* g;
+  int dynamic;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+// Weight-streaming decode kernels (small m); false: the shape is not theirs.
+bool launch_gemm_decode(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
+                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);
+// Quantise a small bf16 activation and multiply it in one decode kernel;
+// false: not supported for this shape (quantise, then launch_gemm).
+bool launch_gemm_decode_quantize(const QuantSource& qs, int64_t m, const uint8_t* w_packed, int64_t n, int64_t k,
+                                 void* out, const EpilogueArgs& epi, hipStream_t st);
+
+// Quantise the bf16 activation of qs and multiply: one kernel where
+// launch_gemm_decode_quantize takes the shape, else launch_quantize and
+// launch_gemm.  epi.a_global must be qs.g.
+hipError_t launch_linear(const QuantSource& qs, int64_t m, const uint8_t* w_packed, int64_t n, int64_t k,
+                         void* out, const EpilogueArgs& epi, hipStream_t st);
+
+// The decode weight stream with no arithmetic (roofline reference).
+hipError_t launch_weight_stream_read(const uint8_t* w_packed, int64_t n, int64_t k, uint32_t* sink, hipStream_t st);
+
 // The tiled (prefill) kernels for any m; used for the quantising SiLU*mul epilogue.
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                              int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);

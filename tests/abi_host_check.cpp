@@ -109,6 +109,23 @@ hipError_t launch_gemm_tiled(const uint8_t*, const uint8_t*, int64_t m, const ui
   g_call.epi = epi;
   return hipSuccess;
 }
+hipError_t launch_linear(const QuantSource& qs, int64_t m, const uint8_t*, int64_t n, int64_t k, void*,
+                         const EpilogueArgs& epi, hipStream_t) {
+  record("linear");
+  g_call.m = m;
+  g_call.n = n;
+  g_call.k = k;
+  g_call.epi = epi;
+  g_call.dynamic = qs.dynamic != 0;
+  g_call.rows = qs.ld_x;
+  return hipSuccess;
+}
+hipError_t launch_weight_stream_read(const uint8_t*, int64_t n, int64_t k, uint32_t*, hipStream_t) {
+  record("stream_read");
+  g_call.n = n;
+  g_call.k = k;
+  return hipSuccess;
+}
 hipError_t launch_gdn_recurrence(const GdnArgs& a, hipStream_t) {
   record("gdn");
   g_call.gdn = a;
@@ -193,6 +210,25 @@ int main() {
          NVFP4_EALIGN, NONE);
   EXPECT(gemm_w4a4(B, B, G, 3, A16, nullptr, 64, 64, A16, 1, 64, 0, nullptr), NVFP4_EINVAL, NONE);
 
+  // nvfp4_linear: the quantiser's and the GEMM's rules together
+  auto lin = [&](int64_t m, int64_t n, int64_t k, int64_t ld_x, int epi, const void* x, float* g, uint8_t* codes) {
+    return nvfp4_linear(static_cast<const uint16_t*>(x), m, k, ld_x, g, 1, codes, B, A16, G, n, A16,
+                        NVFP4_OUT_BF16, epi == NVFP4_EPI_SILU_MUL ? n / 2 : n, epi, nullptr);
+  };
+  EXPECT(lin(1, 17408, 5120, 5120, NVFP4_EPI_NONE, X, G, B), 0, "linear");
+  CHECK(g_call.m == 1 && g_call.n == 17408 && g_call.k == 5120 && g_call.dynamic && g_call.rows == 5120 &&
+        g_call.epi.a_global == G && g_call.epi.seg_w_global == G && g_call.epi.segs.off[1] == 17408);
+  EXPECT(lin(8, 34816, 5120, 5128, NVFP4_EPI_SILU_MUL, X, G, B), 0, "linear");
+  CHECK(g_call.epi.silu_mul == 1 && g_call.epi.ld_out == 17408);
+  EXPECT(lin(0, 64, 128, 128, NVFP4_EPI_NONE, X, G, B), 0, NONE);
+  EXPECT(lin(1, 64, 40, 40, NVFP4_EPI_NONE, X, G, B), NVFP4_ESHAPE, NONE);
+  EXPECT(lin(1, 64, 128, 132, NVFP4_EPI_NONE, X, G, B), NVFP4_EALIGN, NONE);    // rows of x 16-byte aligned
+  EXPECT(lin(1, 96, 128, 128, NVFP4_EPI_SILU_MUL, X, G, B), NVFP4_ESHAPE, NONE);
+  EXPECT(lin(1, 64, 128, 128, 4, X, G, B), NVFP4_EINVAL, NONE);
+  EXPECT(lin(1, 64, 128, 128, NVFP4_EPI_NONE, MIS, G, B), NVFP4_EALIGN, NONE);
+  EXPECT(lin(1, 64, 128, 128, NVFP4_EPI_NONE, X, nullptr, B), NVFP4_EINVAL, NONE);
+  EXPECT(lin(1, 64, 128, 128, NVFP4_EPI_NONE, X, G, static_cast<uint8_t*>(MIS)), NVFP4_EALIGN, NONE);
+
   // gemm_w4a4_fused_segments: six modules with gates
   const int64_t offs[7] = {0, 2048, 4096, 10240, 16384, 16432, 16480};
   const int epis[6] = {NVFP4_SEG_NONE, NVFP4_SEG_NONE, NVFP4_SEG_NONE, NVFP4_SEG_NONE, NVFP4_SEG_SIGMOID,
@@ -229,6 +265,12 @@ int main() {
          NVFP4_EUNSUPPORTED, NONE);
   EXPECT(gdn_recurrence(X, 260, X, 256, X, 768, X, 6, X, 6, 10, 2, 6, 128, nullptr, nullptr, A16, 0, 768, nullptr),
          NVFP4_EALIGN, NONE);
+
+  // weight stream reference
+  EXPECT(nvfp4_weight_stream_read(A16, 17408, 5120, static_cast<uint32_t*>(A16), nullptr), 0, "stream_read");
+  CHECK(g_call.n == 17408 && g_call.k == 5120);
+  EXPECT(nvfp4_weight_stream_read(A16, 17408, 5128, static_cast<uint32_t*>(A16), nullptr), NVFP4_ESHAPE, NONE);
+  EXPECT(nvfp4_weight_stream_read(MIS, 17408, 5120, static_cast<uint32_t*>(A16), nullptr), NVFP4_EALIGN, NONE);
 
   // status strings
   for (int s = 0; s >= -6; --s) CHECK(nvfp4_status_string(s) != nullptr && strlen(nvfp4_status_string(s)) > 0);

@@ -37,6 +37,7 @@ def lib():
 def test_header_declares_the_four_entry_points_and_helpers():
     fns = declared_functions()
     for name in ("nvfp4_quantize", "nvfp4_e2m1_encode", "nvfp4_pack_weights", "gemm_w4a4", "gemm_w4a4_fused_segments",
+                 "nvfp4_linear", "nvfp4_weight_stream_read",
                  "gemm_w4a4_silu_mul_quantize", "gdn_recurrence", "nvfp4_packed_weight_bytes",
                  "nvfp4_unpack_weights_linear",
                  "nvfp4_status_string", "nvfp4_last_hip_error"):
