@@ -117,7 +117,7 @@ DECODE_BYTES = DECODE_W_BYTES + 5120 * 9 // 16 + 17408 * 2
 
 
 OUTER_EVENTS = ("prefill", "decode_all")
-INNER_EVENTS = ("gdn", "gate_up", "down", "decode")
+INNER_EVENTS = ("gdn", "gate_up", "down")
 
 
 def step(torch, B, S, it, ev, inner=True):
@@ -145,11 +145,8 @@ def step(torch, B, S, it, ev, inner=True):
     rec("down", 1)
     outer("prefill", 1)
     outer("decode_all", 0)
-    B.nvfp4_quantize(S["dec_A"], S["qd_g"], True, S["qd_codes"], S["qd_scales"])
-    rec("decode", 0)
-    B.gemm_w4a4(S["qd_codes"], S["qd_scales"], S["qd_g"], S["dec_packed"][it % DECODE_COPIES], S["dec_g"],
-                17408, 5120, out=S["dec_out"])
-    rec("decode", 1)
+    B.nvfp4_linear(S["dec_A"], S["dec_packed"][it % DECODE_COPIES], S["dec_g"], 17408, out=S["dec_out"],
+                   a_global=S["qd_g"], a_codes=S["qd_codes"], a_scales=S["qd_scales"])
     outer("decode_all", 1)
 
 
@@ -183,10 +180,23 @@ def _replay_us(torch, g, calls, reps=3):
 
 def decode_sweep(torch, B, S, iters=64):
     """Decode GEMM time at each M, from HIP-graph replays of `iters` back-to-back launches over the
-    rotating weight copies (a Python launch loop would measure the host, not the kernel).  Each
-    replayed output is checked bit-for-bit against an eager launch of the same call."""
+    rotating weight copies (a Python launch loop would measure the host, not the kernel): gemm_w4a4 on an
+    already quantised activation (GEMM only), and nvfp4_linear on the bf16 activation (quantize + GEMM;
+    one kernel at M = 1).  Each replayed output is checked bit-for-bit against an eager launch.  The
+    weight stream with no arithmetic (nvfp4_weight_stream_read, the decode kernel's loads and launch
+    shape) is timed the same way: the measured ceiling for these GEMMs."""
     from nvfp4_w4a4_gemm_quantize_amd import inputs
-    out = {}
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def reads():
+        for i in range(iters):
+            B.nvfp4_weight_stream_read(S["dec_packed"][i % DECODE_COPIES], 17408, 5120, sink)
+
+    g0 = _graph(torch, reads)
+    stream_us = _replay_us(torch, g0, iters, reps=5)
+    del g0
+    out = {"stream_read_us": round(stream_us, 2), "stream_read_GBps": round(DECODE_W_BYTES / stream_us / 1e3, 1),
+           "stream_read_hbm_frac": round(DECODE_W_BYTES / stream_us / 1e3 / PEAK_HBM_GBPS, 3)}
     for M in inputs.DECODE_M:
         a = dev_bf16(torch, inputs.decode(M, weights=False)["A"])
         qc, qs, qg = B.nvfp4_quantize(a)
@@ -199,19 +209,20 @@ def decode_sweep(torch, B, S, iters=64):
             for i in range(iters):
                 B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
 
-        def quant_gemms():
+        def linears():
             for i in range(iters):
-                B.nvfp4_quantize(a, qg, True, qc, qs)
-                B.gemm_w4a4(qc, qs, qg, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, 5120, out=y)
+                B.nvfp4_linear(a, S["dec_packed"][i % DECODE_COPIES], S["dec_g"], 17408, out=y, a_global=qg,
+                               a_codes=qc, a_scales=qs)
 
-        g1, g2 = _graph(torch, gemms), _graph(torch, quant_gemms)
-        us = _replay_us(torch, g1, iters)
+        g1, g2 = _graph(torch, gemms), _graph(torch, linears)
+        us = _replay_us(torch, g1, iters, reps=5)
         same = bool(torch.equal(y, y_eager))
-        us_q = _replay_us(torch, g2, iters)
+        us_q = _replay_us(torch, g2, iters, reps=5)
         same = same and bool(torch.equal(y, y_eager))
         nbytes = DECODE_W_BYTES + M * (5120 * 9 // 16) + M * 17408 * 2
         out["M%d" % M] = {"gemm_us": round(us, 2), "weight_GBps": round(DECODE_W_BYTES / us / 1e3, 1),
                           "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 3),
+                          "gemm_over_stream_read": round(us / stream_us, 3),
                           "quantize_plus_gemm_us": round(us_q, 2),
                           "tflops": round(2 * M * 17408 * 5120 / us / 1e6, 2),
                           "graph_replay_matches_eager": same}
@@ -222,15 +233,84 @@ def decode_sweep(torch, B, S, iters=64):
 def decode_summary(dur, sweep):
     """The M = 1 decode figures: from the graph replays of the sweep (back-to-back launches, no
     event between kernels) when it ran, else from the timed steps' events.  The in-step event
-    timings are reported beside them: events right around a 12 us kernel add their own delay."""
-    in_step = {"gemm_us": round(dur["decode"] * 1e3, 2), "quantize_plus_gemm_us": round(dur["decode_all"] * 1e3, 2)}
+    timing of the decode part (nvfp4_linear: quantize + GEMM in one kernel) is reported beside them."""
+    in_step = {"quantize_plus_gemm_us": round(dur["decode_all"] * 1e3, 2)}
     if sweep:
         us, us_q, src = sweep["M1"]["gemm_us"], sweep["M1"]["quantize_plus_gemm_us"], "graph replay (decode sweep, M=1)"
     else:
-        us, us_q, src = in_step["gemm_us"], in_step["quantize_plus_gemm_us"], "timed steps, events around the kernels"
-    return {"M": 1, "gemm_us": us, "weight_GBps": round(DECODE_W_BYTES / us / 1e3, 1),
-            "hbm_frac": round(DECODE_BYTES / us / 1e3 / PEAK_HBM_GBPS, 4), "quantize_plus_gemm_us": us_q,
-            "source": src, "in_step_events": in_step, "sweep": sweep}
+        us, us_q, src = None, in_step["quantize_plus_gemm_us"], "timed steps, events around the decode part"
+    res = {"M": 1, "gemm_us": us, "quantize_plus_gemm_us": us_q, "source": src, "in_step_events": in_step,
+           "sweep": sweep}
+    if us is not None:
+        res.update({"weight_GBps": round(DECODE_W_BYTES / us / 1e3, 1),
+                    "hbm_frac": round(DECODE_BYTES / us / 1e3 / PEAK_HBM_GBPS, 4)})
+    if sweep:
+        res["stream_read_us"] = sweep["stream_read_us"]
+        res["gemm_over_stream_read"] = sweep["M1"]["gemm_over_stream_read"]
+    return res
+
+
+def linear_config(torch, B, reps=20):
+    """The single linear layer, prefill (M = 2048, N = K = 5120, bf16 out): quantize A (dynamic g) +
+    GEMM, and the GEMM alone, from events around `reps` back-to-back launches."""
+    from nvfp4_w4a4_gemm_quantize_amd import inputs
+    d = inputs.linear()
+    a = dev_bf16(torch, d["A"])
+    packed, wg = B.nvfp4_pack_weights(dev_bf16(torch, d["W"]))
+    qc, qs, qg = B.nvfp4_quantize(a)
+    y = torch.empty((2048, 5120), dtype=torch.bfloat16, device="cuda")
+
+    def time_us(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    t_g, t_q = [], []
+    for _ in range(3):
+        t_g.append(time_us(lambda: B.gemm_w4a4(qc, qs, qg, packed, wg, 5120, 5120, out=y)))
+        t_q.append(time_us(lambda: B.nvfp4_linear(a, packed, wg, 5120, out=y, a_global=qg, a_codes=qc, a_scales=qs)))
+    t_g, t_q = min(t_g), min(t_q)
+    flop = 2 * 2048 * 5120 * 5120
+    return {"M": 2048, "N": 5120, "K": 5120, "gemm_us": round(t_g, 1), "tflops": round(flop / t_g / 1e6, 1),
+            "mfma_frac": round(flop / t_g / 1e6 / PEAK_F16_TFLOPS, 4), "quantize_plus_gemm_us": round(t_q, 1),
+            "tflops_with_quantize": round(flop / t_q / 1e6, 1)}
+
+
+def quantizer_rates(torch, B, reps=20):
+    """nvfp4_quantize with a dynamic global scale on the path's three activation shapes.  Algorithmic
+    bytes: 2 B read + 0.5625 B written per element (codes + E4M3 scales); the amax pre-pass reads the
+    tensor once more (2 B per element), given separately."""
+    out = {}
+    for name, (r, c) in (("A_4096x5120", (4096, 5120)), ("h_4096x17408", (4096, 17408)), ("A_1x5120", (1, 5120))):
+        x = (torch.randn((r, c), device="cuda") * 3).to(torch.bfloat16)
+        g = torch.empty(1, dtype=torch.float32, device="cuda")
+        codes = torch.empty((r, c // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((r, c // 16), dtype=torch.uint8, device="cuda")
+        fn = lambda: B.nvfp4_quantize(x, g, True, codes, scales)
+        fn()
+        torch.cuda.synchronize()
+        best = 1e9
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / reps)
+        n = r * c
+        algo = n * 2 + n * 9 // 16
+        out[name] = {"us": round(best, 2), "algorithmic_bytes": algo, "GBps": round(algo / best / 1e3, 1),
+                     "hbm_frac": round(algo / best / 1e3 / PEAK_HBM_GBPS, 3),
+                     "GBps_incl_amax_pass": round((algo + 2 * n) / best / 1e3, 1)}
+        del x, codes, scales
+    return out
 
 
 def cpu_baseline(target_s):
@@ -515,13 +595,16 @@ def main():
     gemm_ms = dur["gdn"] + dur["gate_up"] + dur["down"]
     achieved = prefill_flop / (gemm_ms * 1e-3) / 1e12
     sweep = None if args.no_decode_sweep else decode_sweep(torch, B, S)
+    progress("decode sweep done")
+    linear2 = linear_config(torch, B)
+    quant = quantizer_rates(torch, B)
+    progress("single linear layer and quantizer rates timed")
     fused_mlp = mlp_fused(torch, B, S)
     repairs = gdn_repairs(torch, B, S)
     recurrence = gdn_recurrence_run(torch, B, S)
     bf16_ctx = bf16_library_context(torch)
     progress("fused MLP, GDN repairs, the recurrence and the bf16 library context timed")
     traffic = measured_traffic()
-    progress("decode sweep done")
     if args.copy_probe_mib > 0:
         # Untimed plain device copy of known size: the reference point that scales the HBM byte counters.
         nb = args.copy_probe_mib << 20
@@ -561,6 +644,8 @@ def main():
         "prefill_ms": {k: round(dur[k], 4) for k in ("prefill", "gdn", "gate_up", "down")},
         "prefill_ms_with_inner_events": round(prefill_instrumented_ms, 4),
         "decode": decode_summary(dur, sweep),
+        "linear_M2048": linear2,
+        "quantizer": quant,
         "mlp_fused_h_quantize": fused_mlp,
         "gdn_scale_repairs": repairs,
         "gdn_recurrence": recurrence,

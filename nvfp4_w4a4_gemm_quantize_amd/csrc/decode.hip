@@ -547,10 +547,8 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
   // other half's, across the wave), then its data tiles, two products in
   // flight.
   auto super_tile = [&](int64_t ks, const Slot& S) __attribute__((always_inline)) {
-    const uint32_t o0 = (uint32_t)__shfl_xor((int)S.s.x, 32, 64);
-    const uint32_t o1 = (uint32_t)__shfl_xor((int)S.s.y, 32, 64);
-    const uint32_t ws[kSuperTiles] = {h == 0 ? S.s.x : o0, h == 0 ? S.s.y : o1, h == 0 ? o0 : S.s.x,
-                                      h == 0 ? o1 : S.s.y};
+    const uint2 sx = lane_halves(S.s.x), sy = lane_halves(S.s.y);
+    const uint32_t ws[kSuperTiles] = {sx.x, sy.x, sx.y, sy.y};
     const int64_t kt0 = ks * kSuperTiles;
     if (kt0 + kSuperTiles <= KT) {            // the common case: four data tiles
       Prod P[2];
@@ -636,10 +634,11 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
 // The decode kernels' weight stream with no arithmetic: one workgroup of four
 // waves per 32-column slab, each wave reading its share of the slab's
 // super-tiles (four 16-byte code loads and one 8-byte scale load per lane per
-// super-tile, non-temporal) with R super-tiles in flight, exactly as the FP4
-// decode kernel does.  The words are folded into one value that is stored
-// only if it equals a constant, so no load is dead.  Its time is the practical
-// HBM ceiling of the decode GEMM's access pattern.
+// super-tile, non-temporal), as the FP4 decode kernel does, with R = 5: every
+// load of a wave (a whole K = 5120 share) in flight at once, the fastest depth
+// measured for this pattern.  The words are folded into one value that is
+// stored only if it equals a constant, so no load is dead.  Its time is the
+// practical HBM ceiling of the decode GEMM's access pattern.
 template <int R>
 __global__ void __launch_bounds__(256) weight_stream_read_kernel(const uint8_t* __restrict__ w_packed, int64_t k,
                                                                  uint32_t* __restrict__ sink) {
@@ -673,9 +672,13 @@ __global__ void __launch_bounds__(256) weight_stream_read_kernel(const uint8_t* 
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+#ifndef NVFP4_STREAM_READ_RING
+#define NVFP4_STREAM_READ_RING 5
+#endif
 hipError_t launch_weight_stream_read(const uint8_t* w_packed, int64_t n, int64_t k, uint32_t* sink, hipStream_t st) {
   const int64_t slabs = (n + kTileN - 1) / kTileN;
-  hipLaunchKernelGGL((weight_stream_read_kernel<2>), dim3((unsigned)slabs), dim3(256), 0, st, w_packed, k, sink);
+  hipLaunchKernelGGL((weight_stream_read_kernel<NVFP4_STREAM_READ_RING>), dim3((unsigned)slabs), dim3(256), 0, st,
+                     w_packed, k, sink);
   return hipGetLastError();
 }
 

@@ -14,8 +14,10 @@
 // column r of W at 8 K positions chosen by h.  Because a lane's 16 packed
 // bytes hold 32 consecutive K values, sub-step s of a 64-wide K tile uses the
 // lane's dword s: K positions 32h + 8s .. +7 -- the same set for A and W, so
-// the contraction is over every K exactly once.  The 16 accumulators of lane
-// l hold rows 8*(j/4) + 4h + (j%4) of column r.
+// the contraction is over every K exactly once.  The product is taken as
+// W . A^T (mfma_rows), so the 16 accumulators of lane l hold output row r,
+// columns 8q + 4h + e (accumulator 4q + e): four runs of four consecutive
+// columns, stored straight from registers.
 #include "epilogue.h"
 #include "kernels.h"
 #include "nvfp4_device.h"
@@ -23,49 +25,53 @@
 namespace nvfp4 {
 
 
+// True when output columns [c0, c1] (clamped to n - 1) lie in one segment
+// without a gate: one alpha then serves the whole tile.  Segments are
+// contiguous, so the two end columns decide.
+__device__ __forceinline__ bool columns_uniform(const EpilogueArgs& e, int64_t c0, int64_t c1, int64_t n) {
+  c1 = c1 < n ? c1 : n - 1;
+  int s0 = 0, s1 = 0;
+  for (int s = 1; s < e.segs.num; ++s) {
+    s0 += c0 >= e.segs.off[s];
+    s1 += c1 >= e.segs.off[s];
+  }
+  return s0 == s1 && e.seg_epi[s0] == 0;
+}
+
 // ------------------------------------------------------ tile epilogue ----
-// Epilogue of a workgroup tile: each 32x32 accumulator fragment of a wave goes
-// through a per-wave LDS staging tile (32 x 33 floats) so that every lane
-// owns 4 rows x 4 consecutive columns; it applies alpha and the column's gate
-// function and stores 4 contiguous outputs per row.  One runtime loop over
-// the fragments keeps the epilogue code single; the fragment to stage is
-// picked by compile-time cases, so the accumulators stay in registers.
+// Epilogue of a workgroup tile, straight from the accumulators (no LDS
+// staging): lane (r, h) of fragment (i, j) holds output row
+// m0 + wave_m*MF*32 + i*32 + r, columns c + 8q + 4h + e of the fragment's 32
+// (accumulator 4q + e).  Each run of four columns gets alpha and its
+// columns' gate functions and is stored as one 8-byte (bf16) or 16-byte
+// (fp32) write.  A tile whose columns all share one ungated segment takes
+// its alpha once (uniform); otherwise each run reads its four columns'
+// entries of the per-column table ctab.
 // col_base: first output column of the workgroup; wave_n's fragment jj covers
 // output columns col_base + (wave_n * NJ + jj) * 32 .. +31.
-// ctab: the workgroup's per-column table (fill_column_table; unused for SiLU*mul).
+// SILU: gate fragment jj and up fragment jj + NF/2 share the layout, so
+// h = silu(gate) * up is formed in registers.  With h_codes set, h is rounded
+// to bf16 and quantised: a 16-column block of h is split between lanes
+// (r, 0) and (r, 1) (8 values each), which exchange their block maximum and
+// their halves of the codes across the wave halves.
 template <int MF, int NF, int WM, int WN, bool SILU>
-__device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* lds, const ColumnEpilogue* ctab,
-                                              int lane, int wave, int wave_m, int wave_n, int64_t m0,
-                                              int64_t col_base, int64_t m, int64_t n, void* out,
-                                              const EpilogueArgs& epi) {
-  constexpr int EPI_STRIDE = 33;
+__device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const ColumnEpilogue* ctab, bool uniform,
+                                              int lane, int wave_m, int wave_n, int64_t m0, int64_t col_base,
+                                              int64_t m, int64_t n, void* out, const EpilogueArgs& epi) {
   constexpr int NJ = SILU ? NF / 2 : NF;
   const int r = lane & 31, h = lane >> 5;
-  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * EPI_STRIDE);
-  const int er = (lane >> 3) * 4, ec = (lane & 7) * 4;   // this lane: rows er..er+3, cols ec..ec+3
-  const float ga = *epi.a_global;
   const bool bf16 = epi.out_bf16 != 0;
   const int64_t ld = epi.ld_out;
   const int64_t ncols = SILU ? n / 2 : n;
 
-  auto stage_frag = [&](floatx16 f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ep[(8 * (e >> 2) + 4 * h + (e & 3)) * EPI_STRIDE + r] = f[e];
-  };
-  auto read_frag = [&](float (&v)[4][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) v[a][b] = ep[(er + a) * EPI_STRIDE + ec + b];
-  };
-  auto store_row = [&](int64_t row, int64_t col0, const float (&v)[4]) __attribute__((always_inline)) {
-    if (row >= m) return;
+  // four consecutive outputs of one row
+  auto store4 = [&](int64_t row, int64_t col0, const float (&v)[4]) __attribute__((always_inline)) {
     const int64_t idx = row * ld + col0;
     if (col0 + 3 < ncols && (idx & 3) == 0) {
       if (bf16) {
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = pk;
       } else {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = make_float4(v[0], v[1], v[2], v[3]);
@@ -77,84 +83,86 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], uint8_t* 
     }
   };
 
-  const float alpha_silu = SILU ? 1.0f / (ga * epi.seg_w_global[0]) : 0.0f;
-  // SiLU(gate) * up of a fragment pair, in the accumulator layout (the gate
-  // and up fragments share it), so only the result goes through LDS.
-  auto silu_frag = [&](const floatx16& g, const floatx16& u) __attribute__((always_inline)) -> floatx16 {
-    floatx16 hv;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) hv[e] = silu_mul(g[e] * alpha_silu, u[e] * alpha_silu);
-    return hv;
-  };
-  // Quantising SiLU*mul: lane (r, h) takes row r, columns 16h..16h+15 of the
-  // staged fragment -- one whole 16-element block of h.
+  // One runtime loop over the wave's fragments keeps the epilogue code single;
+  // the fragment is copied out of the accumulators by compile-time cases.
+  const float alpha_u = SILU ? 1.0f / (*epi.a_global * epi.seg_w_global[0]) : (uniform ? ctab[0].alpha : 0.0f);
   const bool quant = SILU && epi.h_codes != nullptr;
   const float hg = quant ? *epi.h_global : 0.0f;
-  auto read_block = [&](float (&v)[16]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 16; ++c) v[c] = ep[r * EPI_STRIDE + 16 * h + c];
-  };
   for (int f = 0; f < NJ * MF; ++f) {
     const int jj = f / MF, i = f % MF;
-    const int c0 = (wave_n * NJ + jj) * 32 + ec;
-    const int64_t col0 = col_base + c0;
-    if constexpr (SILU) {
-      if (quant) {
-        float hq[16];
-        wave_lds_order();
-        static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
-          constexpr int F = decltype(c)::value;
-          if (f == F) stage_frag(silu_frag(acc[F % MF][F / MF], acc[F % MF][F / MF + NF / 2]));
-        });
-        wave_lds_order();
-        read_block(hq);
-        // h rounded to bf16 first, then the quantiser's own block arithmetic:
-        // the codes equal those of the bf16 h quantised on its own.
-        uint32_t hb[8];
+    const int64_t row = m0 + wave_m * MF * 32 + i * 32 + r;
+    const int lc = (wave_n * NJ + jj) * 32;                // fragment's first column in the tile
+    float v[16];
+    static_for<0, NJ * MF>([&](auto cc) __attribute__((always_inline)) {
+      constexpr int F = decltype(cc)::value;
+      if (f == F) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          hb[c] = (uint32_t)f32_to_bf16_rne(hq[2 * c]) | ((uint32_t)f32_to_bf16_rne(hq[2 * c + 1]) << 16);
-        const uint4 lo = make_uint4(hb[0], hb[1], hb[2], hb[3]), hi = make_uint4(hb[4], hb[5], hb[6], hb[7]);
-        uint2 codes;
-        const uint32_t S = quantize_block16(lo, hi, hg, &codes);
-        const int64_t row = m0 + wave_m * MF * 32 + i * 32 + r;
-        const int64_t hcol = col_base + (wave_n * NJ + jj) * 32 + 16 * h;
-        // n/2 is a multiple of 32: a fragment's columns are all inside h or all past it
-        if (row < m && hcol < n / 2) {
-          *reinterpret_cast<uint2*>(epi.h_codes + row * (n / 4) + hcol / 2) = codes;
-          epi.h_scales[row * (n / 32) + hcol / 16] = (uint8_t)S;
-          if (epi.h_out) {
-            uint4* dst = reinterpret_cast<uint4*>(epi.h_out + row * (n / 2) + hcol);
-            dst[0] = lo;
-            dst[1] = hi;
+        for (int e = 0; e < 16; ++e) {
+          if constexpr (SILU) v[e] = silu_mul(acc[F % MF][F / MF][e] * alpha_u, acc[F % MF][F / MF + NF / 2][e] * alpha_u);
+          else v[e] = acc[F % MF][F / MF][e];
+        }
+      }
+    });
+    if constexpr (SILU) {
+      const int64_t c0 = col_base + lc;                    // first h column of the fragment
+      if (!quant) {
+        if (row < m) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float w4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+            store4(row, c0 + 8 * q + 4 * h, w4);
           }
         }
         continue;
       }
-    }
-    float v[4][4];
-    wave_lds_order();
-    static_for<0, NJ * MF>([&](auto c) __attribute__((always_inline)) {
-      constexpr int F = decltype(c)::value;
-      if constexpr (SILU) {
-        if (f == F) stage_frag(silu_frag(acc[F % MF][F / MF], acc[F % MF][F / MF + NF / 2]));
-      } else {
-        if (f == F) stage_frag(acc[F % MF][F / MF]);
+      // h in bf16, two values per word: run q holds columns 8q + 4h .. +3
+      uint32_t hb[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hb[q][0] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
+        hb[q][1] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
       }
-    });
-    wave_lds_order();
-    read_frag(v);
-    if constexpr (!SILU) {
+      // block b (columns 16b .. 16b+15) is runs q = 2b, 2b+1 of both lane halves
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const ColumnEpilogue ce = ctab[c0 + b];
+      for (int b = 0; b < 2; ++b) {
+        const uint4 mine = make_uint4(hb[2 * b][0], hb[2 * b][1], hb[2 * b + 1][0], hb[2 * b + 1][1]);
+        const uint2 mh = lane_halves(absmax_bits8(mine));
+        const uint32_t mb = max(mh.x, mh.y);
+        float rr;
+        const uint32_t S = block_scale(mb, hg, &rr);
+        uint32_t x = 0;                                    // codes of my two runs, 16 bits each
+        if (S != 0) x = pack_codes4(mine.x, mine.y, rr) | (pack_codes4(mine.z, mine.w, rr) << 16);
+        const uint2 xh = lane_halves(x);
+        const uint32_t lo = xh.x, hi = xh.y;               // lane half 0's runs, half 1's
+        const uint2 codes = make_uint2((lo & 0xFFFFu) | (hi << 16), (lo >> 16) | (hi & 0xFFFF0000u));
+        const int64_t hcol = c0 + 16 * b;
+        // n/2 is a multiple of 32: a fragment's columns are all inside h or all past it
+        if (h == b && row < m && hcol < n / 2) {
+          *reinterpret_cast<uint2*>(epi.h_codes + row * (n / 4) + hcol / 2) = codes;
+          epi.h_scales[row * (n / 32) + hcol / 16] = (uint8_t)S;
+        }
+      }
+      if (epi.h_out && row < m && c0 < n / 2) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) v[a][b] = apply_epilogue(ce, v[a][b]);
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(epi.h_out + row * (n / 2) + c0 + 8 * q + 4 * h) = make_uint2(hb[q][0], hb[q][1]);
+      }
+    } else {
+      if (row >= m) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = lc + 8 * q + 4 * h;
+        float w4[4];
+        if (uniform) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w4[e] = v[4 * q + e] * alpha_u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w4[e] = apply_epilogue(ctab[c + e], v[4 * q + e]);
+        }
+        store4(row, col_base + c, w4);
       }
     }
-    const int64_t row0 = m0 + wave_m * MF * 32 + i * 32 + er;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) store_row(row0 + a, col0, v[a]);
   }
 }
 
@@ -211,7 +219,7 @@ __device__ __forceinline__ void mma_k64(floatx16 (&acc)[MF][NF], const uint4 (&a
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
-      for (int j = 0; j < NF; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+      for (int j = 0; j < NF; ++j) acc[i][j] = mfma_rows(av[i], bv[j], acc[i][j]);
   }
 }
 
@@ -237,8 +245,7 @@ struct RegShape {
   static constexpr int OFF_BC = OFF_AS + BM * 4;
   static constexpr int OFF_BS = OFF_BC + NTILES * kTileCodeBytes;
   static constexpr int STAGE = OFF_BS + NTILES * 128;
-  static constexpr int EPI_BYTES = WM * WN * 32 * 33 * 4;
-  static constexpr int LDS = (2 * STAGE > EPI_BYTES) ? 2 * STAGE : EPI_BYTES;
+  static constexpr int LDS = 2 * STAGE;
 };
 
 template <int MF, int NF, int WM, int WN, bool SILU>
@@ -402,8 +409,9 @@ gemm_prefill_regs_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __r
     __syncthreads();
   }
 
-  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds, ctab, lane, wave, wave_m, wave_n, m0,
-                                      SILU ? o0 : (int64_t)blockIdx.x * BN, m, n, out, epi);
+  const int64_t cb = SILU ? o0 : (int64_t)blockIdx.x * BN;
+  const bool uniform = !SILU && columns_uniform(epi, cb, cb + BN - 1, n);
+  tile_epilogue<MF, NF, WM, WN, SILU>(acc, ctab, uniform, lane, wave_m, wave_n, m0, cb, m, n, out, epi);
 }
 
 // -------------------------------------- prefill kernel, K % 64 == 0 ----
@@ -484,7 +492,6 @@ struct DmaShape {
   static constexpr int PC_AC = (N_AC + NWAVES - 1) / NWAVES, PC_AS = (N_AS + NWAVES - 1) / NWAVES;
   static constexpr int PC_BC = (N_BC + NWAVES - 1) / NWAVES, PC_BS = (N_BS + NWAVES - 1) / NWAVES;
   static constexpr int LPW = PC_AC + PC_AS + PC_BC + PC_BS;   // DMA instructions per wave per stage
-  static constexpr int EPI_BYTES = NWAVES * 32 * 33 * 4;
   static_assert(BM % 64 == 0 && NTILES % 2 == 0, "A scales move in 64-row groups, W scales in tile pairs");
 };
 
@@ -533,7 +540,6 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[P::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[P::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[NSTAGE > 3 ? P::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_epi[P::EPI_BYTES];
   __shared__ ColumnEpilogue ctab[SILU ? 1 : BN];
   auto buf = [&](auto b) __attribute__((always_inline)) -> uint8_t* {
     constexpr int B = decltype(b)::value;
@@ -674,7 +680,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
 #pragma unroll
       for (int jj = 0; jj < NF; ++jj) {
         const int j = (i & 1) ? NF - 1 - jj : jj;
-        acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+        acc[i][j] = mfma_rows(av[i], bv[j], acc[i][j]);
       }
   };
   // One MFMA, then a few VALU ops, for every MFMA of a sub-step.
@@ -759,8 +765,9 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
     });
   }
 
-  tile_epilogue<MF, NF, WM, WN, SILU>(acc, lds_epi, ctab, lane, wave, wave_m, wave_n, m0,
-                                      SILU ? o0 : (int64_t)bx * BN, m, n, out, epi);
+  const int64_t cb = SILU ? o0 : (int64_t)bx * BN;
+  const bool uniform = !SILU && columns_uniform(epi, cb, cb + BN - 1, n);
+  tile_epilogue<MF, NF, WM, WN, SILU>(acc, ctab, uniform, lane, wave_m, wave_n, m0, cb, m, n, out, epi);
 }
 
 // ------------------------------------------------------------ launcher ----

@@ -93,21 +93,50 @@ __device__ __forceinline__ uint32_t pack_codes8(const uint32_t (&w)[4], float r)
   return c;
 }
 
+// Scale of a block whose largest magnitude is the bf16 pattern mbits (15
+// bits): returns the E4M3 byte S and sets r = g / value(S) (S != 0 only).
+__device__ __forceinline__ uint32_t block_scale(uint32_t mbits, float g, float* r) {
+  const float m = __uint_as_float(mbits << 16);
+  const float t = m / 6.0f;
+  const float u = fminf(t * g, kE4M3Max);
+  const uint32_t S = e4m3_encode_rne(u);
+  *r = S != 0 ? g / e4m3_decode(S) : 0.0f;
+  return S;
+}
+
 __device__ __forceinline__ uint32_t quantize_block16(uint4 lo, uint4 hi, float g, uint2* codes_out) {
-  uint32_t mbits = max(absmax_bits8(lo), absmax_bits8(hi));
-  float m = __uint_as_float(mbits << 16);
-  float t = m / 6.0f;
-  float u = fminf(t * g, kE4M3Max);
-  uint32_t S = e4m3_encode_rne(u);
+  float r;
+  const uint32_t S = block_scale(max(absmax_bits8(lo), absmax_bits8(hi)), g, &r);
   uint2 c = make_uint2(0u, 0u);
   if (S != 0) {
-    float r = g / e4m3_decode(S);
     const uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
     const uint32_t v[4] = {hi.x, hi.y, hi.z, hi.w};
     c = make_uint2(pack_codes8(w, r), pack_codes8(v, r));
   }
   *codes_out = c;
   return S;
+}
+
+// 4 E2M1 codes (16 bits, low nibble first) of two packed bf16 pairs times r.
+__device__ __forceinline__ uint32_t pack_codes4(uint32_t p0, uint32_t p1, float r) {
+  return e2m1_encode_rne_sat(bf16_lo(p0) * r) | (e2m1_encode_rne_sat(bf16_hi(p0) * r) << 4) |
+         (e2m1_encode_rne_sat(bf16_lo(p1) * r) << 8) | (e2m1_encode_rne_sat(bf16_hi(p1) * r) << 12);
+}
+
+// x of both lanes of the pair (l, l ^ 32) at each of them, with one VALU lane
+// swap (gfx950's v_permlane32_swap) instead of an LDS permute: .x is the value
+// from lanes 0-31, .y the value from lanes 32-63.
+__device__ __forceinline__ uint2 lane_halves(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return make_uint2(r[0], r[1]);
+}
+
+// Two floats to packed bf16 (round to nearest even; the low half holds a).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // --------------------------------------------------------- dequantiser ----
@@ -137,6 +166,15 @@ __device__ __forceinline__ half8_t dequant8(uint32_t codes, half2_t sc) {
 
 __device__ __forceinline__ floatx16 mfma32x32x16(half8_t a, half8_t b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// The tiled GEMM's product of an activation fragment (32 rows of A) and a
+// weight fragment (32 rows of W, i.e. 32 output columns), computed as W . A^T
+// so that the result is row-major across lanes: lane l = r + 32h then holds
+// output row r, columns 8q + 4h + e (q = 0..3, e = 0..3) in accumulator
+// 4q + e -- four runs of four consecutive columns of one row.
+__device__ __forceinline__ floatx16 mfma_rows(half8_t a_frag, half8_t w_frag, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(w_frag, a_frag, c, 0, 0, 0);
 }
 
 // ------------------------------------------------------------- outputs ----

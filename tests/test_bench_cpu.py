@@ -33,11 +33,13 @@ def test_workload_flop_and_bytes():
 
 
 def test_decode_headline_prefers_the_graph_replays():
-    dur = {"decode": 0.0157, "decode_all": 0.0201}          # ms, from events around the kernels
-    sweep = {"M1": {"gemm_us": 12.0, "quantize_plus_gemm_us": 14.5}}
+    dur = {"decode_all": 0.0201}                            # ms, from events around the decode part
+    sweep = {"stream_read_us": 8.4,
+             "M1": {"gemm_us": 12.0, "quantize_plus_gemm_us": 14.5, "gemm_over_stream_read": 12.0 / 8.4}}
     d = bench.decode_summary(dur, sweep)
     assert d["gemm_us"] == 12.0 and d["quantize_plus_gemm_us"] == 14.5
     assert abs(d["weight_GBps"] - 50_135_040 / 12.0 / 1e3) < 0.1
-    assert d["in_step_events"] == {"gemm_us": 15.7, "quantize_plus_gemm_us": 20.1}
+    assert d["in_step_events"] == {"quantize_plus_gemm_us": 20.1}
+    assert d["stream_read_us"] == 8.4 and abs(d["gemm_over_stream_read"] - 12.0 / 8.4) < 1e-12
     d0 = bench.decode_summary(dur, None)
-    assert d0["gemm_us"] == 15.7 and d0["sweep"] is None
+    assert d0["gemm_us"] is None and d0["quantize_plus_gemm_us"] == 20.1 and d0["sweep"] is None
