@@ -176,7 +176,7 @@ int nvfp4_unpack_weights_linear(const void* packed, int64_t n, int64_t k,
  *                      (out aligned to its element size).
  *   epilogue           NONE, or SILU_MUL: requires n % 64 == 0 and computes
  *                      out[:, j] = silu(y[:, j]) * y[:, j + n/2].
- * m <= 64 runs a weight-streaming decode kernel (m <= 4 without an epilogue:
+ * m <= 64 runs a weight-streaming decode kernel (m <= 8 without an epilogue:
  * the block-scaled FP4 MFMA on the raw codes with the E4M3 scales applied in
  * FP32; otherwise exact dequantisation to f16 and the f16 MFMA), larger m the
  * tiled prefill kernel; all give results within 1e-5 * sum_k |a*w| * alpha.

@@ -517,15 +517,23 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
   // s_a * s_w applied to its per-block sums.  The MFMA of the next tile goes
   // out before this tile's products are formed, so its latency is covered by
   // this tile's VALU work.
-  struct Prod { floatx16 c; float4 sa[MH]; uint32_t ws; int64_t kt; };
+  // (MR = 8: the A scales are read when the product is applied, which keeps
+  // the kernel within its register budget)
+  constexpr bool kEarlySa = MR <= 4;
+  struct Prod { floatx16 c; float4 sa[kEarlySa ? MH : 1]; uint32_t ws; int64_t kt; };
+  auto load_sa = [&](int64_t kt, int i) __attribute__((always_inline)) {
+    return *reinterpret_cast<const float4*>(s_sa + ((2 * i + h) * KTP + kt) * 4);
+  };
   auto tile_mfma = [&](int64_t kt, const uint4& wb, uint32_t ws, Prod& P) __attribute__((always_inline)) {
     const uint4 a4 = *reinterpret_cast<const uint4*>(smem + kt * (L::RECS * 16) + a_lane);
     const v8i_t av = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
     const v8i_t bv = {(int)wb.x, (int)wb.y, (int)wb.z, (int)wb.w, 0, 0, 0, 0};
     const floatx16 zero = {};
     P.c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, zero, 4, 4, 0, 127, 0, 127);
+    if constexpr (kEarlySa) {
 #pragma unroll
-    for (int i = 0; i < MH; ++i) P.sa[i] = *reinterpret_cast<const float4*>(s_sa + ((2 * i + h) * KTP + kt) * 4);
+      for (int i = 0; i < MH; ++i) P.sa[i] = load_sa(kt, i);
+    }
     P.ws = ws;
     P.kt = kt;
   };
@@ -537,10 +545,11 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
     sw[3] = __builtin_amdgcn_cvt_f32_fp8((int)P.ws, 3);
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      y4[i][0] += (P.sa[i].x * sw[0]) * P.c[4 * i + 0];
-      y4[i][1] += (P.sa[i].y * sw[1]) * P.c[4 * i + 1];
-      y4[i][2] += (P.sa[i].z * sw[2]) * P.c[4 * i + 2];
-      y4[i][3] += (P.sa[i].w * sw[3]) * P.c[4 * i + 3];
+      const float4 sa = kEarlySa ? P.sa[kEarlySa ? i : 0] : load_sa(P.kt, i);
+      y4[i][0] += (sa.x * sw[0]) * P.c[4 * i + 0];
+      y4[i][1] += (sa.y * sw[1]) * P.c[4 * i + 1];
+      y4[i][2] += (sa.z * sw[2]) * P.c[4 * i + 2];
+      y4[i][3] += (sa.w * sw[3]) * P.c[4 * i + 3];
     }
   };
   // A super-tile: row r's scales of all four tiles (this lane's pair and the
@@ -725,10 +734,12 @@ static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const
 #endif
 constexpr int kDecodeFp4Waves = NVFP4_DECODE_FP4_WAVES;
 constexpr int kDecodeFp4Ring = NVFP4_DECODE_FP4_RING;
-constexpr int64_t kDecodeFp4MaxLds = 48 * 1024;   // three workgroups per CU
+// Three workgroups per CU in gfx950's 160 KB of LDS (allocation granules
+// included): enough for eight A rows at K = 5120 (52.5 KB).
+constexpr int64_t kDecodeFp4MaxLds = 52 * 1024 + 512;
 // Staged A blocks per thread on the unrolled staging path: every block of A
 // for K up to 8192 (m <= 2; 6144 when the kernel quantises A) or 5120
-// (m <= 4).  The quantising kernel holds the staged bf16 blocks in registers
+// (m <= 8).  The quantising kernel holds the staged bf16 blocks in registers
 // beside the weight ring, so its ring is shorter.
 template <int MR, bool QUANT>
 constexpr int decode_fp4_stage() {
@@ -766,21 +777,24 @@ static bool launch_decode_fp4(const uint8_t* ac, const uint8_t* as, int64_t m, c
   return true;
 }
 
-// The FP4 path covers plain (non-SILU) GEMMs with m <= 4 (wider tiles of rows
-// or a second, gate/up, slab exceed its register budget).
+// The FP4 path covers plain (non-SILU) GEMMs with m <= 8 (a second, gate/up,
+// slab exceeds its register budget; so do eight rows when it quantises A).
 template <bool QUANT>
 static bool try_decode_fp4(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
                            int64_t k, void* out, const EpilogueArgs& epi, const QuantSource& qs, hipStream_t st) {
   if (epi.silu_mul) return false;
   if (m <= 2) return launch_decode_fp4<2, QUANT>(ac, as, m, w, n, k, out, epi, qs, st);
   if (m <= 4) return launch_decode_fp4<4, QUANT>(ac, as, m, w, n, k, out, epi, qs, st);
+  if constexpr (!QUANT) {
+    if (m <= 8) return launch_decode_fp4<8, false>(ac, as, m, w, n, k, out, epi, qs, st);
+  }
   return false;
 }
 
 bool launch_gemm_decode(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                         int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   const QuantSource none{};
-  if (m <= 4 && try_decode_fp4<false>(a_codes, a_scales, m, w_packed, n, k, out, epi, none, st)) return true;
+  if (m <= 8 && try_decode_fp4<false>(a_codes, a_scales, m, w_packed, n, k, out, epi, none, st)) return true;
   // The f16 decode kernel moves A in 16-byte chunks (32 elements): K % 32 == 16
   // runs the register-staged tile kernel, which reads A per 16-element block.
   if (m > 64 || k % 32 != 0) return false;

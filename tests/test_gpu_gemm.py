@@ -112,17 +112,22 @@ def decode_weight_prepared():
     return w_bits, cw, sw, np.float32(g)
 
 
-# The FP4-MFMA decode kernel (m <= 4) and the branches around it: two and four
-# rows per MFMA (m = 2: the second row of the two-row kernel is stored; m = 3, 4:
-# the four-row kernel), the general A staging loop (more A records than the
-# unrolled staging covers: m = 3, 4 at K = 5120, m <= 2 at K >= 8192), and the
-# f16 decode kernel that takes over when the A records exceed the LDS budget.
+# The FP4-MFMA decode kernel (m <= 8) and the branches around it: two, four and
+# eight rows per MFMA (m = 2: the second row of the two-row kernel is stored;
+# m = 3, 4: the four-row kernel; m = 5..8: the eight-row kernel, whose A scales
+# are read late), compile-time super-tile counts (K = 5120, 4096) and the
+# run-time count (K = 3072), the general A staging loop (more A records than
+# the unrolled staging covers: m <= 2 at K >= 8192), and the f16 decode kernel
+# that takes over when the A records exceed the LDS budget.
 @pytest.mark.parametrize("M,N,K,out", [
     (2, 17408, 5120, "bf16"), (3, 17408, 5120, "bf16"), (4, 17408, 5120, "bf16"),   # the decode config's W
     (2, 1000, 5120, "f32"), (3, 1000, 5120, "f32"), (4, 1000, 5120, "f32"),         # ragged N
     (1, 5120, 17408, "f32"), (2, 5120, 17408, "bf16"),     # K = 17408: general staging loop, 2-row kernel
     (1, 96, 8192, "f32"), (2, 200, 9216, "f32"),
     (3, 640, 17408, "f32"), (4, 640, 17408, "bf16"),       # 4-row records exceed LDS: f16 decode kernel
+    (5, 17408, 5120, "bf16"), (8, 17408, 5120, "bf16"), (7, 1000, 5120, "f32"),      # eight-row kernel
+    (6, 640, 4096, "f32"), (8, 200, 3072, "bf16"),
+    (8, 96, 6144, "f32"), (5, 5120, 17408, "bf16"),       # 8-row records exceed LDS: f16 decode kernel
 ])
 def test_small_m_decode_paths(gpu_lib, M, N, K, out):
     rng = np.random.default_rng(M * 7919 + N + K)
@@ -146,10 +151,10 @@ def test_small_m_decode_paths(gpu_lib, M, N, K, out):
     check_gemm(gpu_out_f64(y), yr, br, out == "bf16", "decode %dx%dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("M", [2, 3, 4, 6, 8])
 def test_fused_segments_small_m_long_k(gpu_lib, M):
     """Fused segments with sigmoid and decay gates through the FP4-MFMA decode
-    kernel at m = 2..4 and K = 5120, over a ragged N with six modules."""
+    kernel at m = 2..8 and K = 5120, over a ragged N with six modules."""
     rng = np.random.default_rng(500 + M)
     K = 5120
     widths = [256, 256, 384, 96, 48, 48]
