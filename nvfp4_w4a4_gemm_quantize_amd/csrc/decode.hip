@@ -306,9 +306,12 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 // slot as soon as its tile is multiplied.  The waves' partial sums are added
 // in LDS in a fixed order.
 //
-// A is staged once per workgroup into LDS: one 16-byte operand record per
-// (tile, block, row) plus one zero record per tile (for lanes whose MFMA row
-// is empty), and the A block scales as FP32.  Its source is either the
+// A is staged once per workgroup into LDS: one 8-byte record (a block's 16
+// codes) per (tile, block, row) plus one zero record per tile (for lanes
+// whose MFMA row is empty), and the A block scales as E4M3 bytes, a lane's
+// rows of a tile side by side (one LDS read per tile; the scales are widened
+// to FP32 in registers).  Each lane places its record in the half of its
+// 16-byte operand that its block occupies.  Its source is either the
 // quantizer's codes and scales, or (QUANT) the bf16 activation itself: every
 // workgroup then computes the tensor's amax and the global scale, and
 // quantises the blocks with the quantizer's own routine (bit-identical to
@@ -319,9 +322,9 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 template <int MR>
 struct Fp4DecodeLds {
-  static constexpr int RECS = 4 * MR + 1;           // records per K tile (last: zeros)
-  __host__ __device__ static int64_t rec_bytes(int64_t kt_count) { return kt_count * RECS * 16; }
-  __host__ __device__ static int64_t scale_bytes(int64_t kt_count) { return (int64_t)MR * kt_count * 4 * 4; }
+  static constexpr int RECS = 4 * MR + 1;           // 8-byte records per K tile (last: zeros)
+  __host__ __device__ static int64_t rec_bytes(int64_t kt_count) { return kt_count * RECS * 8; }
+  __host__ __device__ static int64_t scale_bytes(int64_t kt_count) { return (int64_t)MR * kt_count * 4; }
 };
 
 // Three workgroups per CU (544 slabs of a 17408-column weight are then all
@@ -366,7 +369,8 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
   const int64_t s0 = NPW > 0 ? (int64_t)NPW * wave : KS * wave / DW;
   const int64_t s1 = NPW > 0 ? s0 + NPW : KS * (wave + 1) / DW;
   const int64_t slast = s1 > 0 ? s1 - 1 : 0;
-  float* s_sa = reinterpret_cast<float*>(smem + L::rec_bytes(KTP));
+  // A scale bytes: tile kt, lane half hh: rows 2i + hh, blocks q at (i * 4 + q)
+  uint8_t* s_sab = smem + L::rec_bytes(KTP);
 
   // ---- A staging, part 1: issue the loads (unconditional: invalid items
   // read offset 0, which always exists, and are zeroed afterwards).  Item q
@@ -434,9 +438,8 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
   float ga;
   auto put = [&](uint32_t mm, uint32_t b, uint2 c, uint32_t S) __attribute__((always_inline)) {
     const uint32_t kt = b >> 2, qq = b & 3;
-    *reinterpret_cast<uint4*>(smem + ((int64_t)kt * L::RECS + qq * MR + mm) * 16) =
-        (qq & 1) ? make_uint4(0u, 0u, c.x, c.y) : make_uint4(c.x, c.y, 0u, 0u);
-    s_sa[((int64_t)mm * KTP + kt) * 4 + qq] = e4m3_decode(S);
+    *reinterpret_cast<uint2*>(smem + ((int64_t)kt * L::RECS + qq * MR + mm) * 8) = c;
+    s_sab[((int64_t)kt * 2 + (mm & 1)) * (MH * 4) + (mm >> 1) * 4 + qq] = (uint8_t)S;
   };
   if constexpr (QUANT) {
     // (the launcher runs QUANT only when every block is one of the SP items)
@@ -499,14 +502,16 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
     }
   }
   for (int64_t kt = t; kt < KTP; kt += NT)
-    *reinterpret_cast<uint4*>(smem + (kt * L::RECS + 4 * MR) * 16) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint2*>(smem + (kt * L::RECS + 4 * MR) * 8) = make_uint2(0u, 0u);
   lds_barrier();
 
   // ---- multiply.  This lane's A operand record within a tile: MFMA row
-  // r = 4*amm + aq holds row amm's block aq, which sits in K half aq / 2.
+  // r = 4*amm + aq holds row amm's block aq, which sits in K half aq / 2 and
+  // within it in the 8-byte half aq % 2.
   const int amm = r >> 2, aq = r & 3;
   const bool a_on = amm < MR && h == (aq >> 1);
-  const uint32_t a_lane = a_on ? (uint32_t)((aq * MR + amm) * 16) : (uint32_t)(4 * MR * 16);
+  const uint32_t a_lane = a_on ? (uint32_t)((aq * MR + amm) * 8) : (uint32_t)(4 * MR * 8);
+  const bool a_hi = (aq & 1) != 0;
   float y4[MH][4];
 #pragma unroll
   for (int i = 0; i < MH; ++i)
@@ -516,40 +521,37 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
   // One tile: its MFMA (issued one tile ahead), then the FP32 scale products
   // s_a * s_w applied to its per-block sums.  The MFMA of the next tile goes
   // out before this tile's products are formed, so its latency is covered by
-  // this tile's VALU work.
-  // (MR = 8: the A scales are read when the product is applied, which keeps
-  // the kernel within its register budget)
-  constexpr bool kEarlySa = MR <= 4;
-  struct Prod { floatx16 c; float4 sa[kEarlySa ? MH : 1]; uint32_t ws; int64_t kt; };
-  auto load_sa = [&](int64_t kt, int i) __attribute__((always_inline)) {
-    return *reinterpret_cast<const float4*>(s_sa + ((2 * i + h) * KTP + kt) * 4);
-  };
+  // this tile's VALU work.  The A scales travel as E4M3 bytes (one word per
+  // row: blocks 0..3).
+  typedef uint32_t sa_words_t __attribute__((ext_vector_type(MH)));
+  struct Prod { floatx16 c; uint32_t sa[MH]; uint32_t ws; };
   auto tile_mfma = [&](int64_t kt, const uint4& wb, uint32_t ws, Prod& P) __attribute__((always_inline)) {
-    const uint4 a4 = *reinterpret_cast<const uint4*>(smem + kt * (L::RECS * 16) + a_lane);
-    const v8i_t av = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
+    const uint2 a2 = *reinterpret_cast<const uint2*>(smem + kt * (L::RECS * 8) + a_lane);
+    const v8i_t av = {a_hi ? 0 : (int)a2.x, a_hi ? 0 : (int)a2.y, a_hi ? (int)a2.x : 0, a_hi ? (int)a2.y : 0,
+                      0, 0, 0, 0};
     const v8i_t bv = {(int)wb.x, (int)wb.y, (int)wb.z, (int)wb.w, 0, 0, 0, 0};
     const floatx16 zero = {};
     P.c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, zero, 4, 4, 0, 127, 0, 127);
-    if constexpr (kEarlySa) {
+    if constexpr (MH == 1) {
+      P.sa[0] = *reinterpret_cast<const uint32_t*>(s_sab + (kt * 2 + h) * 4);
+    } else {
+      const sa_words_t w = *reinterpret_cast<const sa_words_t*>(s_sab + (kt * 2 + h) * (MH * 4));
 #pragma unroll
-      for (int i = 0; i < MH; ++i) P.sa[i] = load_sa(kt, i);
+      for (int i = 0; i < MH; ++i) P.sa[i] = w[i];
     }
     P.ws = ws;
-    P.kt = kt;
   };
   auto tile_acc = [&](const Prod& P) __attribute__((always_inline)) {
-    float sw[4];
-    sw[0] = __builtin_amdgcn_cvt_f32_fp8((int)P.ws, 0);
-    sw[1] = __builtin_amdgcn_cvt_f32_fp8((int)P.ws, 1);
-    sw[2] = __builtin_amdgcn_cvt_f32_fp8((int)P.ws, 2);
-    sw[3] = __builtin_amdgcn_cvt_f32_fp8((int)P.ws, 3);
+    const f32x2_t w01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)P.ws, false);
+    const f32x2_t w23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)P.ws, true);
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      const float4 sa = kEarlySa ? P.sa[kEarlySa ? i : 0] : load_sa(P.kt, i);
-      y4[i][0] += (sa.x * sw[0]) * P.c[4 * i + 0];
-      y4[i][1] += (sa.y * sw[1]) * P.c[4 * i + 1];
-      y4[i][2] += (sa.z * sw[2]) * P.c[4 * i + 2];
-      y4[i][3] += (sa.w * sw[3]) * P.c[4 * i + 3];
+      const f32x2_t a01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)P.sa[i], false);
+      const f32x2_t a23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)P.sa[i], true);
+      y4[i][0] += (a01[0] * w01[0]) * P.c[4 * i + 0];
+      y4[i][1] += (a01[1] * w01[1]) * P.c[4 * i + 1];
+      y4[i][2] += (a23[0] * w23[0]) * P.c[4 * i + 2];
+      y4[i][3] += (a23[1] * w23[1]) * P.c[4 * i + 3];
     }
   };
   // A super-tile: row r's scales of all four tiles (this lane's pair and the
@@ -735,7 +737,7 @@ static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const
 constexpr int kDecodeFp4Waves = NVFP4_DECODE_FP4_WAVES;
 constexpr int kDecodeFp4Ring = NVFP4_DECODE_FP4_RING;
 // Three workgroups per CU in gfx950's 160 KB of LDS (allocation granules
-// included): enough for eight A rows at K = 5120 (52.5 KB).
+// included); eight A rows at K = 5120 take 23.7 KB.
 constexpr int64_t kDecodeFp4MaxLds = 52 * 1024 + 512;
 // Staged A blocks per thread on the unrolled staging path: every block of A
 // for K up to 8192 (m <= 2; 6144 when the kernel quantises A) or 5120
