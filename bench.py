@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     p.add_argument("--no-decode-sweep", action="store_true", help="skip the per-M decode sweep (profiling runs)")
+    p.add_argument("--decode-profile", action="store_true",
+                   help="profiling run of the decode kernels only: the GEMM at M = 1, 8, 32, 64, the one-kernel "
+                        "linear layer at M = 1 and the streaming-read reference, 16 eager launches each, then exit")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -554,6 +557,45 @@ def gdn_recurrence_run(torch, B, S, reps=5):
             "input": "the timed step's fused in-projection output (q, k, v, sigmoid and decay gate columns)"}
 
 
+def copy_probe(torch, mib):
+    """Untimed plain device copy of known size: the reference point that scales the HBM byte counters."""
+    if mib <= 0:
+        return
+    nb = mib << 20
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def decode_profile(torch, B, copy_mib, launches=16):
+    """The decode kernels alone, eagerly, for per-dispatch counters: W = 17408 x 5120 over DECODE_COPIES
+    rotating copies (larger than the 256 MB MALL together), A at M = 1, 8, 32, 64."""
+    from nvfp4_w4a4_gemm_quantize_amd import inputs
+    d = inputs.decode(1)
+    p, wg = B.nvfp4_pack_weights(dev_bf16(torch, d["W"]))
+    copies = [p] + [p.clone() for _ in range(DECODE_COPIES - 1)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(launches):
+        B.nvfp4_weight_stream_read(copies[i % DECODE_COPIES], 17408, 5120, sink)
+    for M in (1, 8, 32, 64):
+        a = dev_bf16(torch, inputs.decode(M, weights=False)["A"])
+        qc, qs, qg = B.nvfp4_quantize(a)
+        y = torch.empty((M, 17408), dtype=torch.bfloat16, device="cuda")
+        for i in range(launches):
+            B.gemm_w4a4(qc, qs, qg, copies[i % DECODE_COPIES], wg, 17408, 5120, out=y)
+        if M == 1:
+            for i in range(launches):
+                B.nvfp4_linear(a, copies[i % DECODE_COPIES], wg, 17408, out=y, a_global=qg, a_codes=qc, a_scales=qs)
+    torch.cuda.synchronize()
+    copy_probe(torch, copy_mib)
+    progress("decode profile launches done")
+    print(json.dumps({"decode_profile": {"launches_per_kernel": launches, "M": [1, 8, 32, 64], "N": 17408,
+                                         "K": 5120, "weight_copies": DECODE_COPIES}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -566,6 +608,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.load()
+    if args.decode_profile:
+        decode_profile(torch, B, args.copy_probe_mib)
+        return
     S = setup(torch, B)
     progress("inputs packed and resident (%.1f s)" % S["setup_s"])
     for i in range(args.warmup):
@@ -605,15 +650,7 @@ def main():
     bf16_ctx = bf16_library_context(torch)
     progress("fused MLP, GDN repairs, the recurrence and the bf16 library context timed")
     traffic = measured_traffic()
-    if args.copy_probe_mib > 0:
-        # Untimed plain device copy of known size: the reference point that scales the HBM byte counters.
-        nb = args.copy_probe_mib << 20
-        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_probe(torch, args.copy_probe_mib)
     result = {
         "metric": METRIC,
         "value": round(value, 2),

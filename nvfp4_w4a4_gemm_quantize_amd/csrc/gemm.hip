@@ -22,6 +22,8 @@
 #include "kernels.h"
 #include "nvfp4_device.h"
 
+#include <cmath>
+
 namespace nvfp4 {
 
 
@@ -788,6 +790,15 @@ static int cu_count() {
   return v;
 }
 
+// A tail piece (the tile cut into ry row bands and rx column bands) must
+// itself be a valid DMA tile: whole fragments, 64-row A scale groups, weight
+// tiles in pairs, and (SiLU*mul) matching gate and up halves.
+template <int MF, int NF, int WM, int WN, bool SL>
+constexpr bool piece_ok(int ry, int rx) {
+  return MF % ry == 0 && NF % rx == 0 && (WM * (MF / ry) * 32) % 64 == 0 && (WN * (NF / rx)) % 2 == 0 &&
+         (!SL || (rx == 1 && NF % 2 == 0));
+}
+
 template <int MF, int NF, int WM, int WN>
 static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
                            int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
@@ -819,7 +830,9 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
       const int (*c)[2] = epi.silu_mul ? silu_cuts : cuts;
       const int nc = epi.silu_mul ? 2 : 4;
       for (int i = 0; i < nc; ++i)
-        if (rem * c[i][0] * c[i][1] <= cus) {
+        if (rem * c[i][0] * c[i][1] <= cus &&
+            (epi.silu_mul ? piece_ok<MF, NF, WM, WN, true>(c[i][0], c[i][1])
+                          : piece_ok<MF, NF, WM, WN, false>(c[i][0], c[i][1]))) {
           ry = c[i][0];
           rx = c[i][1];
           break;
@@ -835,22 +848,30 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
   hipLaunchKernelGGL((gemm_prefill_dma_kernel<MFP, NFP, WM, WN, NS, SL>), GRID, block, 0, st, ac, as, m, w, n, \
                      k, out, epi, MAP)
     if (epi.silu_mul) {
-      NVFP4_LAUNCH_PIECE(MF, NF, true, dim3((unsigned)nbig), big);
-      if (ry == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF, true, tail_grid, tail);
-      if (ry == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF, true, tail_grid, tail);
+      if constexpr (piece_ok<MF, NF, WM, WN, true>(1, 1)) {
+        NVFP4_LAUNCH_PIECE(MF, NF, true, dim3((unsigned)nbig), big);
+        if constexpr (piece_ok<MF, NF, WM, WN, true>(2, 1))
+          if (ry == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF, true, tail_grid, tail);
+        if constexpr (piece_ok<MF, NF, WM, WN, true>(4, 1))
+          if (ry == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF, true, tail_grid, tail);
+      }
     } else {
       NVFP4_LAUNCH_PIECE(MF, NF, false, dim3((unsigned)nbig), big);
-      if (ry == 2 && rx == 1) NVFP4_LAUNCH_PIECE(MF / 2, NF, false, tail_grid, tail);
-      if (ry == 2 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF / 2, false, tail_grid, tail);
-      if (ry == 4 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 4, NF / 2, false, tail_grid, tail);
-      if (ry == 4 && rx == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF / 4, false, tail_grid, tail);
+      if constexpr (piece_ok<MF, NF, WM, WN, false>(2, 1))
+        if (ry == 2 && rx == 1) NVFP4_LAUNCH_PIECE(MF / 2, NF, false, tail_grid, tail);
+      if constexpr (piece_ok<MF, NF, WM, WN, false>(2, 2))
+        if (ry == 2 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF / 2, false, tail_grid, tail);
+      if constexpr (piece_ok<MF, NF, WM, WN, false>(4, 2))
+        if (ry == 4 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 4, NF / 2, false, tail_grid, tail);
+      if constexpr (piece_ok<MF, NF, WM, WN, false>(4, 4))
+        if (ry == 4 && rx == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF / 4, false, tail_grid, tail);
     }
 #undef NVFP4_LAUNCH_PIECE
-  } else {
-    if (epi.silu_mul)
+  } else if (epi.silu_mul) {
+    if constexpr (NF % 2 == 0)
       hipLaunchKernelGGL((gemm_prefill_regs_kernel<MF, NF, WM, WN, true>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
-    else
-      hipLaunchKernelGGL((gemm_prefill_regs_kernel<MF, NF, WM, WN, false>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
+  } else {
+    hipLaunchKernelGGL((gemm_prefill_regs_kernel<MF, NF, WM, WN, false>), grid, block, 0, st, ac, as, m, w, n, k, out, epi);
   }
 }
 
@@ -872,9 +893,35 @@ hipError_t launch_linear(const QuantSource& qs, int64_t m, const uint8_t* w_pack
   return launch_gemm(qs.codes, qs.scales, m, w_packed, n, k, out, epi, st);
 }
 
+// Plain GEMMs choose between 256 x 256 tiles and 128 x 320 tiles (five
+// column fragments per wave) by the rounds of one-workgroup-per-CU waves each
+// needs: a 128 x 320 tile is 0.625 of the work of a 256 x 256 one, done at
+// kNarrowEff of its rate (measured: 0.87); a 256 x 256 grid that leaves a
+// partial last round pays about 0.4 of a round for its cut tail.  2048 x 5120
+// (160 wide tiles on 256 CUs, or exactly 256 narrow ones) measured 121 ->
+// 103 us with narrow tiles; 4096 x 5120 (1.25 rounds of wide tiles, or
+// exactly 2 of narrow ones) stays wide: 590 against 619 us.
+#ifndef NVFP4_PREFILL_NARROW
+#define NVFP4_PREFILL_NARROW 1
+#endif
+constexpr double kNarrowEff = 0.85;
+static bool narrow_tiles(int64_t m, int64_t n, const EpilogueArgs& epi) {
+  if (NVFP4_PREFILL_NARROW == 0 || epi.silu_mul) return false;
+  if (NVFP4_PREFILL_NARROW == 2) return true;
+  const double cus = (double)cu_count();
+  const double wide = (double)(((m + 255) / 256) * ((n + 255) / 256));
+  const double narrow = (double)(((m + 127) / 128) * ((n + 319) / 320));
+  const double r_wide = wide <= cus ? 1.0 : std::floor(wide / cus) + (std::fmod(wide, cus) > 0 ? 0.4 : 0.0);
+  const double r_narrow = std::ceil(narrow / cus) * 0.625 / kNarrowEff;
+  return r_narrow < r_wide;
+}
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
-  if (!launch_gemm_decode(a_codes, a_scales, m, w_packed, n, k, out, epi, st))
+  if (launch_gemm_decode(a_codes, a_scales, m, w_packed, n, k, out, epi, st)) return hipGetLastError();
+  if (narrow_tiles(m, n, epi))
+    launch_prefill<2, 5, 2, 2>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
+  else
     launch_prefill<NVFP4_PREFILL_TILE>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
   return hipGetLastError();
 }

@@ -88,6 +88,9 @@ def test_unit_scales_give_the_exact_integer_product(gpu_lib):
     (512, 35712, 256, "f32"),    # 280 tiles: the last 24 as 8 pieces of 64x128
     (512, 38336, 256, "bf16"),   # 300 tiles: the last 44 as quarters (128x128)
     (512, 46040, 256, "f32"),    # 360 tiles: the last 104 as half-height tiles; ragged N
+    # 128x320 tiles (five column fragments per wave), chosen when they need fewer rounds:
+    (384, 65617, 256, "bf16"),   # 618 tiles: two rounds, the last 106 as 212 half-height pieces; ragged N
+    (2048, 5120, 320, "f32"),    # exactly one round of 256 tiles
 ])
 def test_gemm_matches_oracle_everywhere(gpu_lib, M, N, K, out):
     rng = np.random.default_rng(M * 1000003 + N * 101 + K)
