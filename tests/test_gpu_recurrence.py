@@ -12,7 +12,7 @@ initial state, bf16 output, run-to-run identity, near-total resets in some
 chunks (which run the unscaled state update while the rest run the scaled
 one); at the full head layout (16 key / 48 value heads) over 4096 tokens.
 Mechanism: noise of 10% injected into keys, values and both gates at every
-step leaves the output error at a flat plateau over 32768 tokens; a random
+step leaves the output error level (no growth with position) over 32768 tokens; a random
 state impulse (values zero) is forgotten, its output falling by 100x within
 a few thousand steps even with no decay at all (pure overwriting) and faster
 with the decay gates.  The same curves from the oracle over a shorter horizon
