@@ -647,8 +647,9 @@ gemm_decode_fp4_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __res
 // super-tiles (four 16-byte code loads and one 8-byte scale load per lane per
 // super-tile, non-temporal), as the FP4 decode kernel does, with R = 5: every
 // load of a wave (a whole K = 5120 share) in flight at once, the fastest depth
-// measured for this pattern.  The words are folded into one value that is
-// stored only if it equals a constant, so no load is dead.  Its time is the
+// measured for this pattern.  Each lane folds the words of its super-tiles
+// into one value (XOR) that is stored only if it equals a constant, so no
+// load is dead and a planted word can show that it was read.  Its time is the
 // practical HBM ceiling of the decode GEMM's access pattern.
 template <int R>
 __global__ void __launch_bounds__(256) weight_stream_read_kernel(const uint8_t* __restrict__ w_packed, int64_t k,
@@ -673,8 +674,11 @@ __global__ void __launch_bounds__(256) weight_stream_read_kernel(const uint8_t* 
         v[u][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + t * kTileCodeBytes + lane * 16));
       sc[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p + kSuperScaleOff + lane * 8));
     }
+    // fold only the slots that hold the wave's own super-tiles: a slot
+    // clamped onto the last one repeats its words, which would cancel
 #pragma unroll
     for (int u = 0; u < R; ++u) {
+      if (j + u >= s1) continue;
       acc ^= sc[u][0] ^ sc[u][1];
 #pragma unroll
       for (int t = 0; t < kSuperTiles; ++t) acc ^= v[u][t][0] ^ v[u][t][1] ^ v[u][t][2] ^ v[u][t][3];
