@@ -180,6 +180,61 @@ def test_fused_segments_small_m_long_k(gpu_lib, M):
     assert_within(gpu_out_f64(y), ref, tol, "fused segments M=%d K=%d" % (M, K))
 
 
+
+# The f16 decode kernel (8 < m <= 64) over many slabs: 257 to 768 32-column
+# slabs (ragged N at 257 and 376), one, two and five K groups of 256 per wave
+# range, one and two row fragments, rows 9..64.
+@pytest.mark.parametrize("M,N,K,out", [
+    (9, 8200, 256, "f32"), (33, 10240, 1024, "bf16"), (48, 12010, 768, "f32"),
+    (17, 17408, 5120, "bf16"), (64, 17408, 5120, "f32"), (40, 24576, 512, "bf16"),
+    (64, 9000, 1280, "f32"), (31, 9000, 1280, "bf16"),
+])
+def test_f16_decode_many_slabs(gpu_lib, M, N, K, out):
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    a = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    a[:, rng.choice(K, 3, replace=False)] *= 50
+    a_bits = inputs.f32_to_bf16_bits(a)
+    if (N, K) == (17408, 5120):
+        w_bits, cw, sw, gw = decode_weight_prepared()
+    else:
+        w_bits = inputs.f32_to_bf16_bits((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
+        gw = OQ.dynamic_global_scale(w_bits)
+        cw, sw = oracle_quantize_rows(w_bits, gw)
+    gs = np.array([gw], np.float32)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits)
+    assert np.float32(host(wg)[0]) == gs[0]
+    y = gpu_lib.gemm_w4a4(ac, asc, ag, packed, wg, N, K,
+                          out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    ca, sa, ga = OQ.quantize(a_bits)
+    yr, br = oracle_gemm_rows(ca, sa, ga, cw, sw, OG.column_global(N, [0, N], gs))
+    check_gemm(gpu_out_f64(y), yr, br, out == "bf16", "f16 decode %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [16, 40, 64])
+def test_fused_segments_f16_decode(gpu_lib, M):
+    """Fused segments with sigmoid and decay gates through the f16 decode
+    kernel: six modules over 262 slabs, ragged N."""
+    rng = np.random.default_rng(900 + M)
+    K = 512
+    widths = [4096, 2048, 2016, 96, 48, 44]
+    offs = list(np.cumsum([0] + widths))
+    N = offs[-1]
+    f = [1.0, 8.0, 2.0, 4.0, 1.5, 3.0]
+    w = np.concatenate([rng.standard_normal((n, K)) * fs / np.sqrt(K) for n, fs in zip(widths, f)]).astype(np.float32)
+    a = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    a[:, rng.choice(K, 3, replace=False)] *= 50
+    a_bits, w_bits = inputs.f32_to_bf16_bits(a), inputs.f32_to_bf16_bits(w)
+    a_log = (rng.standard_normal(44) * 0.5).astype(np.float32)
+    dt = (rng.standard_normal(44) * 0.5).astype(np.float32)
+    ac, asc, ag, packed, wg = gpu_prepare(gpu_lib, a_bits, w_bits, offs)
+    epis = ["none", "none", "none", "none", "sigmoid", "gdn_decay"]
+    y = gpu_lib.gemm_w4a4_fused_segments(ac, asc, ag, packed, N, K, offs, wg, epis, f32(a_log), f32(dt),
+                                         out_dtype=torch.bfloat16)
+    ca, sa, ga, cw, sw, gs, gcol = oracle_prepare(a_bits, w_bits, offs)
+    yr, br = OG.gemm(ca, sa, ga, cw, sw, gcol)
+    ref, tol = gdn_reference(yr, br, offs, a_log, dt)
+    assert_within(gpu_out_f64(y), ref, tol, "fused segments f16 decode M=%d" % M)
+
 # K = 16 (mod 32): a valid NVFP4 K whose last 32-element half holds one block.
 @pytest.mark.parametrize("M,N,K", [(1, 96, 48), (3, 64, 80), (8, 100, 48), (20, 256, 5136), (100, 96, 80),
                                    (300, 160, 5136), (2, 512, 5136)])
