@@ -111,7 +111,9 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
  * quantisation rule above): sign bit 3 = the sign bit of q[i] (-0 gives 8),
  * magnitude rounded to the nearest of 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to
  * the even code, magnitudes above 6 giving 6 (code 7).  NVFP4's element type
- * (aipulsen page, second paragraph).
+ * (aipulsen page, second paragraph).  The kernels convert two values per
+ * instruction into one of four byte positions; here values 2j and 2j+1 share
+ * one conversion at position j % 4, so every slot the quantizer uses runs.
  *
  *   q      device float [n], 4-byte aligned; finite values (NaN unspecified).
  *   n      >= 0 (0 enqueues nothing).

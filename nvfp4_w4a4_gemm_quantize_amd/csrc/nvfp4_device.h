@@ -54,26 +54,18 @@ __device__ __forceinline__ float e4m3_decode(uint32_t s) {
 }
 
 // --------------------------------------------------------------- E2M1 ----
-// 4-bit E2M1 code of an FP32 value q: sign bit 3 (the sign of q, also for
-// -0), magnitude |q| rounded to the nearest of 0, .5, 1, 1.5, 2, 3, 4, 6 with
-// ties to the even code, and every magnitude above 6 giving 6.  Integer
-// arithmetic on the bit pattern, no conversion instruction:
-//   |q| < 1   the grid is uniform with step .5, so the code is rint(2|q|)
-//             (RNE; 2|q| is exact), i.e. 0, 1 or 2 (2 is the code of 1.0);
-//   |q| >= 1  the significand is rounded to one bit with ties to even, the
-//             carry moving into the exponent; the code is 2 + 2e + m for
-//             |q| = 2^e (1 + m/2), clamped to 7 (saturation).
-__device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float q) {
-  const uint32_t b = __float_as_uint(q);
-  const uint32_t a = b & 0x7FFFFFFFu;
-  uint32_t c;
-  if (a < 0x3F800000u) {
-    c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
-  } else {
-    const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
-    c = min((r >> 22) - 252u, 7u);        // (biased exponent 127 + e) * 2 + m - 254 + 2
-  }
-  return c | ((b >> 28) & 8u);
+// E2M1 codes of FP32 values by gfx950's FP32 -> FP4 conversion with a unit
+// scale: two codes per instruction (a in the low nibble) into byte SEL of
+// old.  Each code: sign bit 3 = the sign of the value (-0 gives 8), magnitude
+// rounded to the nearest of 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even
+// code, magnitudes above 6 giving 6.  That this is the instruction's rounding
+// is checked on the GPU through nvfp4_e2m1_encode (the same instruction in
+// both operand slots and all four byte positions) against the closed form
+// over every fp32 near each decision point and grid value, and a strided
+// sweep of all finite values, both signs.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
 // ---------------------------------------------------- block quantizer ----
@@ -82,15 +74,12 @@ __device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float q) {
 //   u = min((m/6)*g, 448); S = E4M3 RNE(u); S == 0 -> codes 0;
 //   r = g / value(S); code_i = E2M1 RNE, saturating, of x_i * r, with the sign of x_i.
 // Every step is one IEEE FP32 operation (correctly rounded division, a
-// correctly rounded product q = x_i * r) followed by the integer E2M1 encoder.
+// correctly rounded product q = x_i * r) followed by the E2M1 conversion.
 __device__ __forceinline__ uint32_t pack_codes8(const uint32_t (&w)[4], float r) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c |= e2m1_encode_rne_sat(bf16_lo(w[i]) * r) << (8 * i);
-    c |= e2m1_encode_rne_sat(bf16_hi(w[i]) * r) << (8 * i + 4);
-  }
-  return c;
+  uint32_t c = e2m1_pair<0>(0u, bf16_lo(w[0]) * r, bf16_hi(w[0]) * r);
+  c = e2m1_pair<1>(c, bf16_lo(w[1]) * r, bf16_hi(w[1]) * r);
+  c = e2m1_pair<2>(c, bf16_lo(w[2]) * r, bf16_hi(w[2]) * r);
+  return e2m1_pair<3>(c, bf16_lo(w[3]) * r, bf16_hi(w[3]) * r);
 }
 
 // Scale of a block whose largest magnitude is the bf16 pattern mbits (15
@@ -119,8 +108,7 @@ __device__ __forceinline__ uint32_t quantize_block16(uint4 lo, uint4 hi, float g
 
 // 4 E2M1 codes (16 bits, low nibble first) of two packed bf16 pairs times r.
 __device__ __forceinline__ uint32_t pack_codes4(uint32_t p0, uint32_t p1, float r) {
-  return e2m1_encode_rne_sat(bf16_lo(p0) * r) | (e2m1_encode_rne_sat(bf16_hi(p0) * r) << 4) |
-         (e2m1_encode_rne_sat(bf16_lo(p1) * r) << 8) | (e2m1_encode_rne_sat(bf16_hi(p1) * r) << 12);
+  return e2m1_pair<1>(e2m1_pair<0>(0u, bf16_lo(p0) * r, bf16_hi(p0) * r), bf16_lo(p1) * r, bf16_hi(p1) * r);
 }
 
 // x of both lanes of the pair (l, l ^ 32) at each of them, with one VALU lane

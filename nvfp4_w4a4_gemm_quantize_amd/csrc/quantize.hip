@@ -168,10 +168,23 @@ unpack_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int64_t 
 // ------------------------------------------------------ E2M1 encoder ----
 // The quantizer's E2M1 encoder applied to caller-given FP32 values, one code
 // (0..15) per byte: exposes the exact device routine for verification.
+// Values 2j and 2j+1 share one conversion (operand slots a and b), written to
+// byte position j % 4, so every slot and position the quantizer uses is run.
 __global__ void __launch_bounds__(kThreads)
 e2m1_encode_kernel(const float* __restrict__ q, int64_t n, uint8_t* __restrict__ codes) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
-    codes[i] = (uint8_t)e2m1_encode_rne_sat(q[i]);
+  const int64_t pairs = (n + 1) / 2;
+  for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < pairs; j += (int64_t)gridDim.x * kThreads) {
+    const float a = q[2 * j], b = 2 * j + 1 < n ? q[2 * j + 1] : 0.0f;
+    uint32_t w;
+    switch (j & 3) {
+      case 0: w = e2m1_pair<0>(0u, a, b); break;
+      case 1: w = e2m1_pair<1>(0u, a, b) >> 8; break;
+      case 2: w = e2m1_pair<2>(0u, a, b) >> 16; break;
+      default: w = e2m1_pair<3>(0u, a, b) >> 24; break;
+    }
+    codes[2 * j] = (uint8_t)(w & 0xFu);
+    if (2 * j + 1 < n) codes[2 * j + 1] = (uint8_t)((w >> 4) & 0xFu);
+  }
 }
 
 // ---------------------------------------------------------- launchers ----
@@ -236,7 +249,7 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* c
 }
 
 hipError_t launch_e2m1_encode(const float* q, int64_t n, uint8_t* codes, hipStream_t st) {
-  hipLaunchKernelGGL(e2m1_encode_kernel, dim3(grid_for(n, 8192)), dim3(kThreads), 0, st, q, n, codes);
+  hipLaunchKernelGGL(e2m1_encode_kernel, dim3(grid_for((n + 1) / 2, 8192)), dim3(kThreads), 0, st, q, n, codes);
   return hipGetLastError();
 }
 

@@ -52,7 +52,8 @@ def _fp32_neighbourhood(x, span):
 
 
 def test_e2m1_encoder_around_every_decision_point(gpu_lib):
-    """The device E2M1 encoder (the one the quantizer applies to x * g / s)
+    """The device E2M1 encoder (the hardware conversion the quantizer applies
+    to x * g / s, run in both operand slots and all four byte positions)
     against the oracle's closed form (pinned exhaustively on the CPU): every fp32
     within 2^16 ulps of each decision point, within 2^12 ulps of each grid value
     and of 8, a strided sweep over all finite non-negative fp32 patterns
