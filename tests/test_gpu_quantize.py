@@ -70,6 +70,22 @@ def test_e2m1_encoder_around_every_decision_point(gpu_lib):
     assert_bytes_equal(got, want, "E2M1 encoder (%d values)" % q.size)
 
 
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 7, 9, 4097])
+def test_e2m1_encode_odd_lengths_leave_the_tail_alone(gpu_lib, n):
+    """Lengths that end on a half-filled conversion pair and in each byte
+    position: codes[0..n) match the closed form, the bytes past n keep their canary."""
+    from oracle import formats as F
+    rng = np.random.default_rng(n)
+    q = (rng.standard_normal(n) * 4).astype(np.float32)
+    q[::3] = -q[::3]
+    buf = torch.full((n + 16,), 0xA5, dtype=torch.uint8, device="cuda")
+    gpu_lib.nvfp4_e2m1_encode(torch.from_numpy(q).cuda(), buf)
+    got = host(buf)
+    want = F.e2m1_rne_sat(np.abs(q)) | (np.signbit(q).astype(np.uint8) << 3)
+    assert_bytes_equal(got[:n], want, "E2M1 encoder, n=%d" % n)
+    assert np.all(got[n:] == 0xA5), "bytes past n were written"
+
 ACTIVATIONS = {
     "tiny": lambda: inputs.tiny()["A"],
     "linear": lambda: inputs.linear()["A"],
