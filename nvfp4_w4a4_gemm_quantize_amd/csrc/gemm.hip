@@ -85,6 +85,29 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const Col
     }
   };
 
+  // bf16, a whole fragment's 32 columns inside the output and 16-byte aligned
+  // rows: the lane halves trade runs so that each lane stores 8 consecutive
+  // columns at once -- lane (r, 0) columns 16p .. 16p+7, lane (r, 1) columns
+  // 16p+8 .. 16p+15 of run pair p -- two 16-byte stores per fragment
+  // instead of four 8-byte ones.
+#ifndef NVFP4_EPI_PAIRED
+#define NVFP4_EPI_PAIRED 1
+#endif
+  const bool paired_ok = NVFP4_EPI_PAIRED && bf16 && (ld & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  auto store_paired = [&](int64_t row, int64_t c0, const uint2 (&pk)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      // lane h keeps run 2p + h and receives the other half's run 2p + h
+      const uint2 give = h ? pk[2 * p] : pk[2 * p + 1];
+      const uint2 keep = h ? pk[2 * p + 1] : pk[2 * p];
+      const uint2 gx = lane_halves(give.x), gy = lane_halves(give.y);
+      const uint2 got = h ? make_uint2(gx.x, gy.x) : make_uint2(gx.y, gy.y);
+      const uint4 w = h ? make_uint4(got.x, got.y, keep.x, keep.y) : make_uint4(keep.x, keep.y, got.x, got.y);
+      if (row < m)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + row * ld + c0 + 16 * p + 8 * h) = w;
+    }
+  };
+
   // One runtime loop over the wave's fragments keeps the epilogue code single;
   // the fragment is copied out of the accumulators by compile-time cases.
   const float alpha_u = SILU ? 1.0f / (*epi.a_global * epi.seg_w_global[0]) : (uniform ? ctab[0].alpha : 0.0f);
@@ -108,7 +131,12 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const Col
     if constexpr (SILU) {
       const int64_t c0 = col_base + lc;                    // first h column of the fragment
       if (!quant) {
-        if (row < m) {
+        if (paired_ok && c0 + 32 <= ncols) {
+          uint2 pk[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pk[q] = make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
+          store_paired(row, c0, pk);
+        } else if (row < m) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float w4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
@@ -150,6 +178,24 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const Col
           *reinterpret_cast<uint2*>(epi.h_out + row * (n / 2) + c0 + 8 * q + 4 * h) = make_uint2(hb[q][0], hb[q][1]);
       }
     } else {
+      if (paired_ok && col_base + lc + 32 <= ncols) {
+        uint2 pk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = lc + 8 * q + 4 * h;
+          float w4[4];
+          if (uniform) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w4[e] = v[4 * q + e] * alpha_u;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w4[e] = apply_epilogue(ctab[c + e], v[4 * q + e]);
+          }
+          pk[q] = make_uint2(pack_bf16x2(w4[0], w4[1]), pack_bf16x2(w4[2], w4[3]));
+        }
+        store_paired(row, col_base + lc, pk);
+        continue;
+      }
       if (row >= m) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
