@@ -41,6 +41,10 @@ __device__ __forceinline__ bool columns_uniform(const EpilogueArgs& e, int64_t c
 }
 
 // ------------------------------------------------------ tile epilogue ----
+#ifndef NVFP4_EPI_PAIRED
+#define NVFP4_EPI_PAIRED 1   // 0: every bf16 run as its own 8-byte store
+#endif
+
 // Epilogue of a workgroup tile, straight from the accumulators (no LDS
 // staging): lane (r, h) of fragment (i, j) holds output row
 // m0 + wave_m*MF*32 + i*32 + r, columns c + 8q + 4h + e of the fragment's 32
@@ -90,9 +94,6 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const Col
   // columns at once -- lane (r, 0) columns 16p .. 16p+7, lane (r, 1) columns
   // 16p+8 .. 16p+15 of run pair p -- two 16-byte stores per fragment
   // instead of four 8-byte ones.
-#ifndef NVFP4_EPI_PAIRED
-#define NVFP4_EPI_PAIRED 1
-#endif
   const bool paired_ok = NVFP4_EPI_PAIRED && bf16 && (ld & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   auto store_paired = [&](int64_t row, int64_t c0, const uint2 (&pk)[4]) __attribute__((always_inline)) {
 #pragma unroll
