@@ -87,31 +87,43 @@ quantize_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int6
 }
 
 // Whole small tensor in one workgroup: amax, g, then the blocks.  Saves two
-// launches for decode-sized activations.
-__global__ void __launch_bounds__(1024)
+// launches for decode-sized activations.  Every thread loads all its blocks
+// (at most kSmallBlocksPerThread) at once and keeps them in registers for
+// the quantisation, so the tensor crosses memory once, in one round trip.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallBlocksPerThread = 4;      // 65,536 elements in 16-element blocks over 1024 threads
+__global__ void __launch_bounds__(kSmallThreads)
 quantize_small_dynamic_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                               float* __restrict__ gout, uint8_t* __restrict__ codes,
                               uint8_t* __restrict__ scales) {
-  __shared__ uint32_t lds[1024 / 64];
-  const int64_t vpr = cols >> 3;
-  const int64_t nvec = rows * vpr;
+  __shared__ uint32_t lds[kSmallThreads / 64];
+  const uint32_t bpr = (uint32_t)(cols >> 4), nblk = (uint32_t)rows * bpr;
+  uint4 lo[kSmallBlocksPerThread], hi[kSmallBlocksPerThread];
   uint32_t m = 0;
-  for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
-    const int64_t r = i / vpr, c = (i % vpr) << 3;
-    m = max(m, absmax_bits8(*reinterpret_cast<const uint4*>(x + r * ld + c)));
+#pragma unroll
+  for (int j = 0; j < kSmallBlocksPerThread; ++j) {
+    // unconditional loads (past the end: the last block again, left out of the max)
+    const uint32_t q = min(threadIdx.x + (uint32_t)j * kSmallThreads, nblk - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)(q / bpr) * ld + ((q % bpr) << 4));
+    lo[j] = src[0];
+    hi[j] = src[1];
   }
+#pragma unroll
+  for (int j = 0; j < kSmallBlocksPerThread; ++j)
+    if (threadIdx.x + (uint32_t)j * kSmallThreads < nblk) m = max(m, max(absmax_bits8(lo[j]), absmax_bits8(hi[j])));
   m = block_max_u32(m, lds);
   const float amax = __uint_as_float(m << 16);
   const float g = amax > 0.0f ? kGlobalNumerator / amax : 1.0f;
   if (threadIdx.x == 0) *gout = g;
-  const int64_t bpr = cols >> 4;
-  for (int64_t i = threadIdx.x; i < rows * bpr; i += blockDim.x) {
-    const int64_t r = i / bpr, b = i % bpr;
-    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + (b << 4));
-    uint2 c;
-    uint32_t S = quantize_block16(src[0], src[1], g, &c);
-    *reinterpret_cast<uint2*>(codes + i * 8) = c;
-    scales[i] = (uint8_t)S;
+#pragma unroll
+  for (int j = 0; j < kSmallBlocksPerThread; ++j) {
+    const uint32_t q = threadIdx.x + (uint32_t)j * kSmallThreads;
+    if (q < nblk) {
+      uint2 c;
+      const uint32_t S = quantize_block16(lo[j], hi[j], g, &c);
+      *reinterpret_cast<uint2*>(codes + (int64_t)q * 8) = c;
+      scales[q] = (uint8_t)S;
+    }
   }
 }
 
@@ -194,14 +206,14 @@ static int grid_for(int64_t items, int64_t cap) {
   return (int)(g < 1 ? 1 : g);
 }
 
-constexpr int64_t kSmallElems = 65536;   // one-workgroup dynamic path
+constexpr int64_t kSmallElems = (int64_t)kSmallThreads * kSmallBlocksPerThread * 16;   // one-workgroup dynamic path
 constexpr int kMaxPartials = 1024;
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* g,
                            bool dynamic, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   const int64_t nblk = rows * (cols / 16);
   if (dynamic && rows * cols <= kSmallElems) {
-    hipLaunchKernelGGL(quantize_small_dynamic_kernel, dim3(1), dim3(1024), 0, st,
+    hipLaunchKernelGGL(quantize_small_dynamic_kernel, dim3(1), dim3(kSmallThreads), 0, st,
                        x, rows, cols, ld, g, codes, scales);
     return hipGetLastError();
   }
