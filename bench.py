@@ -46,6 +46,7 @@ PEAK_F16_TFLOPS = 2500.0      # MI355X dense f16/bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0     # dense FP4 MFMA (context only: NVFP4's E4M3 scales do not fit it)
 PEAK_HBM_GBPS = 8000.0
 DECODE_COPIES = 8
+CONFIGS = ("step", "linear", "quantizer", "decode", "recurrence")
 
 
 def parse():
@@ -61,6 +62,11 @@ def parse():
                         "linear layer at M = 1 and the streaming-read reference, 16 eager launches each, then exit")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--config", choices=CONFIGS, default="step",
+                   help="step (default): the timed step and every measurement beside it, one JSON line in the "
+                        "bench contract; the others run one measurement alone and print {config, result}: "
+                        "linear (M=2048 N=K=5120 layer), quantizer (the three activation shapes), decode (the "
+                        "M sweep and the streaming-read reference), recurrence (4096 tokens x 48 heads)")
     return p.parse_args()
 
 
@@ -596,6 +602,20 @@ def decode_profile(torch, B, copy_mib, launches=16):
                                          "K": 5120, "weight_copies": DECODE_COPIES}}), flush=True)
 
 
+def single_config(torch, B, name):
+    """One measurement on its own (bench.py --config NAME)."""
+    if name == "linear":
+        return linear_config(torch, B)
+    if name == "quantizer":
+        return quantizer_rates(torch, B)
+    S = setup(torch, B)
+    if name == "decode":
+        return decode_sweep(torch, B, S)
+    # the recurrence takes the fused in-projection's output of one step as its input
+    step(torch, B, S, 0, None)
+    return gdn_recurrence_run(torch, B, S)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -610,6 +630,9 @@ def main():
     B.load()
     if args.decode_profile:
         decode_profile(torch, B, args.copy_probe_mib)
+        return
+    if args.config != "step":
+        print(json.dumps({"config": args.config, "result": single_config(torch, B, args.config)}), flush=True)
         return
     S = setup(torch, B)
     progress("inputs packed and resident (%.1f s)" % S["setup_s"])

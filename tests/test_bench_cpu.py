@@ -43,3 +43,13 @@ def test_decode_headline_prefers_the_graph_replays():
     assert d["stream_read_us"] == 8.4 and abs(d["gemm_over_stream_read"] - 12.0 / 8.4) < 1e-12
     d0 = bench.decode_summary(dur, None)
     assert d0["gemm_us"] is None and d0["quantize_plus_gemm_us"] == 20.1 and d0["sweep"] is None
+
+
+def test_config_switch_choices_and_single_gpu_rule():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "nope"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "invalid choice" in r.stderr and r.stdout == ""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "linear", "--gpus", "2"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "--gpus 1" in r.stderr and r.stdout == ""
+    assert bench.CONFIGS[0] == "step"          # the default keeps the one-line bench contract
