@@ -77,7 +77,11 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
         for (int e = 0; e < 16; ++e) part[i][j][q][e] = 0.0f;
 
   // Per-lane constant offsets; per-tile bases are wave-uniform (scalar).
-  const uint32_t w_lane = lane * 16, ws_lane = r * 8 + 2 * h;
+  // The W scale load takes the whole aligned word of row r's four block
+  // scales (a 16-bit load would be widened by a VALU op that waits for it --
+  // at the loop latch, for the group just issued); lane half h picks its pair
+  // at use.
+  const uint32_t w_lane = lane * 16, ws_lane = r * 8, ws_shift = 16 * h;
   // A in LDS (ALDS): 16-byte chunk (kt, s, hh, row) at ((kt*4 + s)*2 + hh)*(m+1) + row,
   // row m of every group is zero; lanes of rows >= m read it.
   const int64_t a_rows = m + 1;
@@ -102,7 +106,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 #pragma unroll
     for (int j = 0; j < NS; ++j) {                                 // tile bases are wave-uniform
       T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile_code_off(slab[j], kt, KS) + w_lane);
-      T.bs[j] = *reinterpret_cast<const uint16_t*>(w_packed + tile_scale_off(slab[j], kt, KS, 0) + ws_lane);
+      T.bs[j] = *reinterpret_cast<const uint32_t*>(w_packed + tile_scale_off(slab[j], kt, KS, 0) + ws_lane);
     }
   };
   // A of one tile for the non-ALDS paths: codes (16 bytes: K half h of row
@@ -125,7 +129,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const uint32_t cw = s == 0 ? T.b[j].x : s == 1 ? T.b[j].y : s == 2 ? T.b[j].z : T.b[j].w;
-        bv[j] = dequant8(cw, scale_pair_f16(scale_byte(T.bs[j], s)));
+        bv[j] = dequant8(cw, scale_pair_f16((T.bs[j] >> (ws_shift + 8 * (s >> 1))) & 0xFFu));
       }
 #pragma unroll
       for (int i = 0; i < MFD; ++i)
@@ -141,22 +145,36 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   auto load_agroup = [&](int64_t g0, AGroup& G) __attribute__((always_inline)) {
     if constexpr (GA) {
       g0 = g0 < kt1 - 4 ? g0 : kt1 - 4;              // groups past the wave's range: never multiplied
+      // Rows past m read row m - 1 instead (unconditional loads: a load under
+      // a branch makes the compiler wait for it at the join).  Row i of the
+      // MFMA's A operand only reaches output row i, and rows >= m are never
+      // stored.
+      // (loaded as an ext_vector: a copy of the uint4 struct from global
+      // memory goes through a stack object)
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      auto ld = [](const uint8_t* p) __attribute__((always_inline)) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+        return make_uint4(v[0], v[1], v[2], v[3]);
+      };
 #pragma unroll
       for (int i = 0; i < MFD; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t row = i * 32 + 8 * j + (lane >> 3);
-          G.c[i][j] = ld16(a_codes + row * a_row_bytes + g0 * 32 + (lane & 7) * 16, row < m);
+          const int64_t row = min(i * 32 + 8 * j + (lane >> 3), m - 1);
+          G.c[i][j] = ld(a_codes + row * a_row_bytes + g0 * 32 + (lane & 7) * 16);
         }
-        const int64_t row = i * 32 + r;
-        G.s[i] = ld16(a_scales + row * a_row_scales + g0 * 4, row < m);
+        const int64_t row = min(i * 32 + r, m - 1);
+        G.s[i] = ld(a_scales + row * a_row_scales + g0 * 4);
       }
     }
   };
+  // A group's loads all go out before the next multiply starts (the
+  // scheduler would otherwise move some behind that group's waits).
   auto load_group = [&](int64_t g0, Tile (&T)[U], AGroup& G) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) load(g0 + u, T[u]);
     load_agroup(g0, G);
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto compute_group = [&](int64_t g0, const Tile (&T)[U], const AGroup& G) __attribute__((always_inline)) {
     if constexpr (GA) {
