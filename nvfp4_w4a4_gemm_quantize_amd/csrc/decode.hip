@@ -35,6 +35,14 @@ constexpr int kDecodeGroupA = NVFP4_DECODE_GROUP_A;
 // A staging in dynamic LDS of exactly (m+1)*k*2 bytes): the 544 workgroups of
 // a 17408-column projection are then all resident at once instead of the
 // last few running as a second round.
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format,
+// no swizzle): loads past the range read zero.
+constexpr int kBufferFlags = 0x00020000;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+#ifndef NVFP4_DECODE_W_AUX
+#define NVFP4_DECODE_W_AUX 0
+#endif
+constexpr int kDecodeWAux = NVFP4_DECODE_W_AUX;
 constexpr int kDecodeGroupRow = 144;          // LDS bytes per A row of a group (128 + 16: conflict-free reads)
 constexpr int kDecodeGroupFrag = 32 * kDecodeGroupRow;
 
@@ -46,8 +54,13 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   constexpr int NS = SILU ? 2 : 1;                 // weight slabs per workgroup
   constexpr int NACC = MFD * NS;
   static_assert(!GA || (!ALDS && U == 4), "grouped A fetch: four tiles per load group");
-  __shared__ float s_red[DW - 1][NACC][16][64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_ag[GA ? DW * MFD * kDecodeGroupFrag : 16];
+  // The waves' A-group areas (GA) and the final cross-wave sums share one LDS
+  // buffer: the sums are written only after every wave has left its loop.
+  constexpr int kRedBytes = (DW - 1) * NACC * 16 * 64 * 4;
+  constexpr int kAgBytes = GA ? DW * MFD * kDecodeGroupFrag : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kRedBytes > kAgBytes ? kRedBytes : kAgBytes];
+  uint8_t* const s_ag = s_lds;
+  auto s_red = reinterpret_cast<float (*)[NACC][16][64]>(s_lds);
   extern __shared__ __attribute__((aligned(16))) uint8_t s_a[];    // ALDS: (m+1)*k*2 bytes
 
   const int t = threadIdx.x;
@@ -64,8 +77,9 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   const int64_t kt1 = GA ? (KT / 4) * (wave + 1) / DW * 4 : KT * (wave + 1) / DW;
 
   // Independent accumulators per K sub-step break the MFMA dependency chain
-  // (a single 32x32 output tile would otherwise serialise every MFMA).
-  constexpr int NSUB = 2;
+  // (a single 32x32 output tile would otherwise serialise every MFMA); with
+  // two row fragments their two chains already alternate.
+  constexpr int NSUB = MFD * NS >= 2 ? 1 : 2;
   floatx16 part[MFD][NS][NSUB];
 #pragma unroll
   for (int i = 0; i < MFD; ++i)
@@ -82,6 +96,13 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   // at the loop latch, for the group just issued); lane half h picks its pair
   // at use.
   const uint32_t w_lane = lane * 16, ws_lane = r * 8, ws_shift = 16 * h;
+  // Weight loads: buffer loads over each slab's bytes, a constant lane offset
+  // plus a wave-uniform tile offset (no per-lane 64-bit address arithmetic).
+  __amdgpu_buffer_rsrc_t w_rsrc[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    w_rsrc[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w_packed) + slab[j] * KS * kSuperBytes,
+                                                  (short)0, (int)(KS * kSuperBytes), kBufferFlags);
   // A in LDS (ALDS): 16-byte chunk (kt, s, hh, row) at ((kt*4 + s)*2 + hh)*(m+1) + row,
   // row m of every group is zero; lanes of rows >= m read it.
   const int64_t a_rows = m + 1;
@@ -103,10 +124,12 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
         T.as[i] = ok ? *reinterpret_cast<const uint16_t*>(a_scales + row * a_row_scales + kt * 4 + 2 * h) : 0u;
       }
     }
+    const int code_off = (int)tile_code_off(0, kt, KS), scale_off = (int)tile_scale_off(0, kt, KS, 0);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {                                 // tile bases are wave-uniform
-      T.b[j] = *reinterpret_cast<const uint4*>(w_packed + tile_code_off(slab[j], kt, KS) + w_lane);
-      T.bs[j] = *reinterpret_cast<const uint32_t*>(w_packed + tile_scale_off(slab[j], kt, KS, 0) + ws_lane);
+    for (int j = 0; j < NS; ++j) {                                 // tile offsets are wave-uniform
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc[j], w_lane, code_off, kDecodeWAux);
+      T.b[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      T.bs[j] = __builtin_amdgcn_raw_buffer_load_b32(w_rsrc[j], ws_lane, scale_off, kDecodeWAux);
     }
   };
   // A of one tile for the non-ALDS paths: codes (16 bytes: K half h of row
@@ -142,29 +165,41 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
   // scales for the group's four tiles (16 bytes).
   struct AGroup { uint4 c[GA ? MFD : 1][GA ? 4 : 1]; uint4 s[GA ? MFD : 1]; };
   uint8_t* const ag_base = s_ag + (GA ? wave * MFD * kDecodeGroupFrag : 0);
+  // The group loads are buffer loads against A's extent (m rows): the range
+  // check returns zeros for rows past m, so no clamp is needed, and each load
+  // takes a loop-invariant 32-bit lane offset (which alone carries the row)
+  // plus the group's wave-uniform K offset.  (With clamped 64-bit addresses
+  // the loop ran out of registers at three waves per SIMD, and the spill
+  // reloads waited for every load in flight.)  Row i of the MFMA's A operand
+  // only reaches output row i, and rows >= m are never stored.  The host
+  // keeps m * k / 2 below 2^31.
+  uint32_t ag_off[GA ? MFD : 1][GA ? 4 : 1], as_off[GA ? MFD : 1];
+  const __amdgpu_buffer_rsrc_t ac_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a_codes), (short)0, GA ? (int)(m * a_row_bytes) : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a_scales), (short)0, GA ? (int)(m * a_row_scales) : 0, kBufferFlags);
+  if constexpr (GA) {
+#pragma unroll
+    for (int i = 0; i < MFD; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ag_off[i][j] = (uint32_t)(i * 32 + 8 * j + (lane >> 3)) * (uint32_t)a_row_bytes + (lane & 7) * 16;
+      as_off[i] = (uint32_t)(i * 32 + r) * (uint32_t)a_row_scales;
+    }
+  }
   auto load_agroup = [&](int64_t g0, AGroup& G) __attribute__((always_inline)) {
     if constexpr (GA) {
       g0 = g0 < kt1 - 4 ? g0 : kt1 - 4;              // groups past the wave's range: never multiplied
-      // Rows past m read row m - 1 instead (unconditional loads: a load under
-      // a branch makes the compiler wait for it at the join).  Row i of the
-      // MFMA's A operand only reaches output row i, and rows >= m are never
-      // stored.
-      // (loaded as an ext_vector: a copy of the uint4 struct from global
-      // memory goes through a stack object)
-      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-      auto ld = [](const uint8_t* p) __attribute__((always_inline)) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+      const int cg = (int)(g0 * 32), sg = (int)(g0 * 4);   // wave-uniform
+      auto ld = [](__amdgpu_buffer_rsrc_t rs, uint32_t off, int soff) __attribute__((always_inline)) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, soff, 0);
         return make_uint4(v[0], v[1], v[2], v[3]);
       };
 #pragma unroll
       for (int i = 0; i < MFD; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t row = min(i * 32 + 8 * j + (lane >> 3), m - 1);
-          G.c[i][j] = ld(a_codes + row * a_row_bytes + g0 * 32 + (lane & 7) * 16);
-        }
-        const int64_t row = min(i * 32 + r, m - 1);
-        G.s[i] = ld(a_scales + row * a_row_scales + g0 * 4);
+        for (int j = 0; j < 4; ++j) G.c[i][j] = ld(ac_rsrc, ag_off[i][j], cg);
+        G.s[i] = ld(as_rsrc, as_off[i], sg);
       }
     }
   };
@@ -257,6 +292,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
       for (int q = 1; q < NSUB; ++q) acc[i][j] += part[i][j][q];
     }
 
+  if constexpr (GA) __syncthreads();                // other waves may still read their A-group areas
   if (wave > 0) {
 #pragma unroll
     for (int i = 0; i < MFD; ++i)
@@ -721,7 +757,8 @@ static void launch_decode_kernel(const uint8_t* ac, const uint8_t* as, int64_t m
   const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
   const unsigned lds = ALDS ? (unsigned)((m + 1) * ((k + kTileK - 1) / kTileK) * kTileK * 2) : 0u;
   // grouped A fetch: whole 4-tile groups per row (k % 256 == 0) and 16-byte scale loads
-  const bool ga = !ALDS && U == 4 && k % 256 == 0 && (reinterpret_cast<uintptr_t>(as) & 15u) == 0;
+  const bool ga = !ALDS && U == 4 && k % 256 == 0 && (reinterpret_cast<uintptr_t>(as) & 15u) == 0 &&
+                  m * (k / 2) < (int64_t(1) << 31);   // 32-bit lane offsets into A
   if constexpr (!ALDS && U == 4) {
     if (ga) {
       hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, true>), dim3((unsigned)slabs),
@@ -744,7 +781,9 @@ static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const
   } else if constexpr (MFD == 2 && SILU) {
     launch_decode_kernel<2, true, false, 2, 1, 4>(ac, as, m, w, n, k, out, epi, st);
   } else {
-    launch_decode_kernel<MFD, SILU, false, 2, 2, 4>(ac, as, m, w, n, k, out, epi, st);
+    // four waves per slab, three per SIMD: the 2176 waves of a 17408-column
+    // projection are all resident, at most three (a quarter of a slab's K each) per SIMD
+    launch_decode_kernel<MFD, SILU, false, 4, 3, 4>(ac, as, m, w, n, k, out, epi, st);
   }
 }
 
