@@ -282,6 +282,11 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
     }
   }
 
+  // The lane's indices again, from mbcnt rather than kept live across the
+  // loop (at three waves per SIMD that cost three spilled registers per lane).
+  {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int r = lane & 31, h = lane >> 5;
   floatx16 acc[MFD][NS];
 #pragma unroll
   for (int i = 0; i < MFD; ++i)
@@ -338,6 +343,7 @@ gemm_decode_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restric
         if (row < m) store_out(out, bf16, row * epi.ld_out + col, apply_epilogue(ce, acc[i][0][e]));
       }
   }
+  }  // the block of the recomputed lane indices
 }
 
 // ------------------------------------------------ decode kernel, FP4 MFMA ----
@@ -751,14 +757,18 @@ hipError_t launch_weight_stream_read(const uint8_t* w_packed, int64_t n, int64_t
   return hipGetLastError();
 }
 
+// Grouped A fetch: whole 4-tile groups per row (k % 256 == 0), 16-byte scale
+// loads and 32-bit lane offsets into A.
+static bool decode_group_a_ok(const uint8_t* as, int64_t m, int64_t k) {
+  return k % 256 == 0 && (reinterpret_cast<uintptr_t>(as) & 15u) == 0 && m * (k / 2) < (int64_t(1) << 31);
+}
+
 template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U>
 static void launch_decode_kernel(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
                                  int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
   const unsigned lds = ALDS ? (unsigned)((m + 1) * ((k + kTileK - 1) / kTileK) * kTileK * 2) : 0u;
-  // grouped A fetch: whole 4-tile groups per row (k % 256 == 0) and 16-byte scale loads
-  const bool ga = !ALDS && U == 4 && k % 256 == 0 && (reinterpret_cast<uintptr_t>(as) & 15u) == 0 &&
-                  m * (k / 2) < (int64_t(1) << 31);   // 32-bit lane offsets into A
+  const bool ga = !ALDS && U == 4 && decode_group_a_ok(as, m, k);
   if constexpr (!ALDS && U == 4) {
     if (ga) {
       hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, true>), dim3((unsigned)slabs),
@@ -780,10 +790,16 @@ static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const
       launch_decode_kernel<1, false, false, 4, 3, 4>(ac, as, m, w, n, k, out, epi, st);
   } else if constexpr (MFD == 2 && SILU) {
     launch_decode_kernel<2, true, false, 2, 1, 4>(ac, as, m, w, n, k, out, epi, st);
+  } else if constexpr (MFD == 2) {
+    if (decode_group_a_ok(as, m, k))
+      // four waves per slab, three per SIMD: the 2176 waves of a 17408-column
+      // projection are all resident, at most three (a quarter of a slab's K each) per SIMD
+      launch_decode_kernel<2, false, false, 4, 3, 4>(ac, as, m, w, n, k, out, epi, st);
+    else
+      // per-tile A fetch: its registers need two waves per SIMD
+      launch_decode_kernel<2, false, false, 2, 2, 4>(ac, as, m, w, n, k, out, epi, st);
   } else {
-    // four waves per slab, three per SIMD: the 2176 waves of a 17408-column
-    // projection are all resident, at most three (a quarter of a slab's K each) per SIMD
-    launch_decode_kernel<MFD, SILU, false, 4, 3, 4>(ac, as, m, w, n, k, out, epi, st);
+    launch_decode_kernel<1, true, false, 2, 2, 4>(ac, as, m, w, n, k, out, epi, st);
   }
 }
 

@@ -183,11 +183,14 @@ def test_fused_segments_small_m_long_k(gpu_lib, M):
 
 # The f16 decode kernel (8 < m <= 64) over many slabs: 257 to 768 32-column
 # slabs (ragged N at 257 and 376), one, two and five K groups of 256 per wave
-# range, one and two row fragments, rows 9..64.
+# range, one and two row fragments, rows 9..64.  K % 256 != 0 (the last rows)
+# takes its per-tile A fetch instead of the grouped one, at one and two row
+# fragments.
 @pytest.mark.parametrize("M,N,K,out", [
     (9, 8200, 256, "f32"), (33, 10240, 1024, "bf16"), (48, 12010, 768, "f32"),
     (17, 17408, 5120, "bf16"), (64, 17408, 5120, "f32"), (40, 24576, 512, "bf16"),
     (64, 9000, 1280, "f32"), (31, 9000, 1280, "bf16"),
+    (31, 1500, 2080, "bf16"), (20, 3000, 1312, "f32"), (48, 1200, 800, "bf16"), (64, 2000, 4128, "f32"),
 ])
 def test_f16_decode_many_slabs(gpu_lib, M, N, K, out):
     rng = np.random.default_rng(M * 31 + N * 7 + K)
