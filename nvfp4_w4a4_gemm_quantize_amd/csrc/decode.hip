@@ -763,21 +763,24 @@ static bool decode_group_a_ok(const uint8_t* as, int64_t m, int64_t k) {
   return k % 256 == 0 && (reinterpret_cast<uintptr_t>(as) & 15u) == 0 && m * (k / 2) < (int64_t(1) << 31);
 }
 
-template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U>
+// GA_ONLY: the caller has checked decode_group_a_ok, so the per-tile-fetch
+// kernel of this shape is never launched (and not instantiated).
+template <int MFD, bool SILU, bool ALDS, int DW, int WPE, int U, bool GA_ONLY = false>
 static void launch_decode_kernel(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
                                  int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   const int64_t slabs = SILU ? (n / 2) / kTileN : (n + kTileN - 1) / kTileN;
   const unsigned lds = ALDS ? (unsigned)((m + 1) * ((k + kTileK - 1) / kTileK) * kTileK * 2) : 0u;
   const bool ga = !ALDS && U == 4 && decode_group_a_ok(as, m, k);
   if constexpr (!ALDS && U == 4) {
-    if (ga) {
+    if (GA_ONLY || ga) {
       hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, true>), dim3((unsigned)slabs),
                          dim3(DW * 64), lds, st, ac, as, m, w, n, k, out, epi);
       return;
     }
   }
-  hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, false>), dim3((unsigned)slabs), dim3(DW * 64),
-                     lds, st, ac, as, m, w, n, k, out, epi);
+  if constexpr (!GA_ONLY)
+    hipLaunchKernelGGL((gemm_decode_kernel<MFD, SILU, ALDS, DW, WPE, U, false>), dim3((unsigned)slabs),
+                       dim3(DW * 64), lds, st, ac, as, m, w, n, k, out, epi);
 }
 
 template <int MFD, bool SILU>
@@ -794,7 +797,7 @@ static void launch_decode(const uint8_t* ac, const uint8_t* as, int64_t m, const
     if (decode_group_a_ok(as, m, k))
       // four waves per slab, three per SIMD: the 2176 waves of a 17408-column
       // projection are all resident, at most three (a quarter of a slab's K each) per SIMD
-      launch_decode_kernel<2, false, false, 4, 3, 4>(ac, as, m, w, n, k, out, epi, st);
+      launch_decode_kernel<2, false, false, 4, 3, 4, true>(ac, as, m, w, n, k, out, epi, st);
     else
       // per-tile A fetch: its registers need two waves per SIMD
       launch_decode_kernel<2, false, false, 2, 2, 4>(ac, as, m, w, n, k, out, epi, st);
