@@ -880,6 +880,8 @@ bool launch_gemm_decode(const uint8_t* a_codes, const uint8_t* a_scales, int64_t
   // The f16 decode kernel moves A in 16-byte chunks (32 elements): K % 32 == 16
   // runs the register-staged tile kernel, which reads A per 16-element block.
   if (m > 64 || k % 32 != 0) return false;
+  // and addresses each weight slab through a buffer descriptor with a 32-bit range
+  if (super_count(k) * kSuperBytes >= (int64_t(1) << 31)) return false;
   if (m <= 32) {
     if (epi.silu_mul) launch_decode<1, true>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
     else launch_decode<1, false>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
