@@ -571,45 +571,65 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU>
-__global__ void __launch_bounds__(WM * WN * 64)
-gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
-                        const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
-                        EpilogueArgs epi, TileMap tmap) {
+// The body of the prefill kernels.  KW == 1: the WM x WN waves share the
+// stage buffers and split the tile.  KW > 1 (split-K, WM = WN = 1): each of
+// the KW waves multiplies the whole tile over its own contiguous range of K
+// super-tiles through a private set of stage buffers (no barrier in the
+// loop), and the partial sums are added through LDS in a fixed wave order.
+template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU, int KW>
+__device__ __forceinline__ void prefill_dma_tile(const uint8_t* __restrict__ a_codes,
+                                                 const uint8_t* __restrict__ a_scales, int64_t m,
+                                                 const uint8_t* __restrict__ w_packed, int64_t n, int64_t k,
+                                                 void* __restrict__ out, const EpilogueArgs& epi, const TileMap& tmap) {
   using P = DmaShape<MF, NF, WM, WN, NSTAGE>;
   constexpr int NWAVES = P::NWAVES, BM = P::BM, BN = P::BN, NTILES = P::NTILES;
+  constexpr bool SK = KW > 1;
+  constexpr int NT = (SK ? KW : NWAVES) * 64;    // threads of the workgroup
   static_assert(NSTAGE == 3 || NSTAGE == 4, "3 or 4 stages");
+  static_assert(!SK || (WM == 1 && WN == 1 && !SILU && KW == NSTAGE && (MF == 2 || MF == 4) && NF % 2 == 0 &&
+                        MF * NF <= 16),
+                "split-K: one wave per K range covers the tile; owners finish whole fragment rows or halves");
   // One LDS object per stage: the compiler can then tell that the DMA into the
   // stage being filled does not alias the reads of the stage being consumed
   // and does not wait for it before those reads.
   // (stage 0 starts 1 KB into its object: an LDS address of exactly 0 lets the
   // compiler fold the offsets into bit operations that lose the alias
   // information the DMA waits rely on)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[P::STAGE + 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[P::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[P::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[NSTAGE > 3 ? P::STAGE : 16];
+  // (split-K: each stage object holds the KW waves' private buffers side by side)
+  constexpr int SW = SK ? KW : 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[SW * P::STAGE + 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[SW * P::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[SW * P::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[NSTAGE > 3 ? SW * P::STAGE : 16];
   __shared__ ColumnEpilogue ctab[SILU ? 1 : BN];
-  auto buf = [&](auto b) __attribute__((always_inline)) -> uint8_t* {
-    constexpr int B = decltype(b)::value;
-    if constexpr (B == 0) return lds_s0 + 1024;
-    else if constexpr (B == 1) return lds_s1;
-    else if constexpr (B == 2) return lds_s2;
-    else return lds_s3;
-  };
 
   const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wave_m = wave / WN, wave_n = wave % WN;
+  const int lw = SK ? 0 : wave;                 // the wave's index within the load and tile split
+  const uint32_t wbuf = SK ? (uint32_t)wave * P::STAGE : 0u;
+  auto buf = [&](auto b) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int B = decltype(b)::value;
+    if constexpr (B == 0) return lds_s0 + 1024 + wbuf;
+    else if constexpr (B == 1) return lds_s1 + wbuf;
+    else if constexpr (B == 2) return lds_s2 + wbuf;
+    else return lds_s3 + wbuf;
+  };
+  const int wave_m = lw / WN, wave_n = lw % WN;
   const int64_t KT = k / kTileK;
   const int64_t KS = super_count(k);
   const int64_t ntiles_total = (n + kTileN - 1) / kTileN;
   int bx, by;
   map_tile(tmap, bx, by);
   const int64_t m0 = (int64_t)by * BM;
+  // split-K: a piece wholly past m or n has nothing to store
+  if constexpr (SK)
+    if (m0 >= m || (int64_t)bx * BN >= n) return;
+  // K steps [kb, ke) of this wave: whole super-tiles (the launcher keeps k % 256 == 0 and KS >= KW)
+  const int64_t kb = SK ? kSuperTiles * (KS * wave / KW) : 0;
+  const int64_t ke = SK ? kSuperTiles * (KS * (wave + 1) / KW) : KT;
   const uint32_t a_row_bytes = (uint32_t)(k / 2), a_row_scales = (uint32_t)(k / 16);
   const int64_t o0 = SILU ? (int64_t)bx * (BN / 2) : 0;
-  if constexpr (!SILU) fill_column_table<BN, NWAVES * 64>(ctab, epi, (int64_t)bx * BN, n);
+  if constexpr (!SILU) fill_column_table<BN, NT>(ctab, epi, (int64_t)bx * BN, n);
 
   auto ntile_of = [&](int tl) -> int64_t {
     int64_t nt;
@@ -636,26 +656,26 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
 #pragma unroll
   for (int i = 0; i < P::LPW; ++i) {
     if (i < I_AS) {
-      const int f = (wave + i * NWAVES) % P::N_AC;
-      src[i] = a_codes;
+      const int f = (lw + i * NWAVES) % P::N_AC;
+      src[i] = a_codes + kb * 32;
       voff[i] = (uint32_t)(row_of(m0 + 32 * f + r) * a_row_bytes) + h * 16;
       dst[i] = f * 1024;
     } else if (i < I_BC) {
-      const int g = (wave + (i - I_AS) * NWAVES) % P::N_AS;
-      src[i] = a_scales;
+      const int g = (lw + (i - I_AS) * NWAVES) % P::N_AS;
+      src[i] = a_scales + kb * 4;
       voff[i] = (uint32_t)(row_of(m0 + 64 * g + lane) * a_row_scales);
       dst[i] = P::OFF_AS + g * 256;
     } else if (i < I_BS) {
-      const int tl = (wave + (i - I_BC) * NWAVES) % P::N_BC;
-      src[i] = w_packed + tile_code_off(ntile_of(tl), 0, KS);
+      const int tl = (lw + (i - I_BC) * NWAVES) % P::N_BC;
+      src[i] = w_packed + tile_code_off(ntile_of(tl), kb, KS);
       voff[i] = lane * 16;
       dst[i] = P::OFF_BC + tl * 1024;
     } else {
-      const int p = (wave + (i - I_BS) * NWAVES) % P::N_BS;
+      const int p = (lw + (i - I_BS) * NWAVES) % P::N_BS;
       // the pair's two tiles (h = 0, 1) differ per lane half: the tile's base
       // offset goes in the lane part
-      const int64_t o0 = tile_scale_off(ntile_of(2 * p), 0, KS, 0);
-      const int64_t o1 = tile_scale_off(ntile_of(2 * p + 1), 0, KS, 0);
+      const int64_t o0 = tile_scale_off(ntile_of(2 * p), kb, KS, 0);
+      const int64_t o1 = tile_scale_off(ntile_of(2 * p + 1), kb, KS, 0);
       src[i] = w_packed + o0;
       voff[i] = (uint32_t)(h ? o1 - o0 : 0) + r * 8;
       dst[i] = P::OFF_BS + p * 256;
@@ -742,7 +762,7 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   auto sync_stage = [&](auto waitn) __attribute__((always_inline)) {
     wait_vmcnt<decltype(waitn)::value>();
     compiler_fence();
-    __builtin_amdgcn_s_barrier();
+    if constexpr (!SK) __builtin_amdgcn_s_barrier();   // split-K: the stage is the wave's own
     compiler_fence();
   };
 
@@ -800,23 +820,110 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
   };
   // Steady state, NSTAGE steps per iteration (compile-time buffers); every step
   // issues a stage, so each waits with NSTAGE-2 stages still in flight.
-  int64_t kt0 = 0;
-  for (; kt0 + 2 * NSTAGE - 1 < KT; kt0 += NSTAGE) {
+  int64_t kt0 = kb;
+  for (; kt0 + 2 * NSTAGE - 1 < ke; kt0 += NSTAGE) {
     static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
       kstep(b, true, true, std::integral_constant<int, P::LPW * (NSTAGE - 2)>{});
     });
   }
   // Tail: the last steps wait for every load in flight.
-  for (; kt0 < KT; kt0 += NSTAGE) {
+  for (; kt0 < ke; kt0 += NSTAGE) {
     static_for<0, NSTAGE>([&](auto b) __attribute__((always_inline)) {
       const int64_t kt = kt0 + decltype(b)::value;
-      if (kt < KT) kstep(b, kt + 1 < KT, kt + NSTAGE < KT, std::integral_constant<int, 0>{});
+      if (kt < ke) kstep(b, kt + 1 < ke, kt + NSTAGE < ke, std::integral_constant<int, 0>{});
     });
   }
 
   const int64_t cb = SILU ? o0 : (int64_t)bx * BN;
   const bool uniform = !SILU && columns_uniform(epi, cb, cb + BN - 1, n);
-  tile_epilogue<MF, NF, WM, WN, SILU>(acc, ctab, uniform, lane, wave_m, wave_n, m0, cb, m, n, out, epi);
+  if constexpr (!SK) {
+    tile_epilogue<MF, NF, WM, WN, SILU>(acc, ctab, uniform, lane, wave_m, wave_n, m0, cb, m, n, out, epi);
+  } else {
+    // Wave v finishes OWN fragments: fragment row v (MF == 4) or half of row
+    // v / 2 (MF == 2).  In G-fragment phases every other wave writes its
+    // partials of v's fragments into stage object v (writer w at slot
+    // w - (w > v)), and v adds the KW partials in wave order 0, 1, ..., KW - 1.
+    // Every wave's last step waited for all of its loads, so after the first
+    // barrier no DMA is left in flight into the stage objects.
+    constexpr int OWN = MF * NF / KW, G = OWN < 2 ? OWN : 2;
+    constexpr int FB = 16 * 64 * 4;                       // bytes of one fragment's partials
+    static_assert((KW - 1) * G * FB <= SW * P::STAGE, "a phase's partials fit one stage object");
+    auto obj = [&](auto v) __attribute__((always_inline)) -> float* {
+      constexpr int V = decltype(v)::value;
+      if constexpr (V == 0) return reinterpret_cast<float*>(lds_s0 + 1024);
+      else if constexpr (V == 1) return reinterpret_cast<float*>(lds_s1);
+      else if constexpr (V == 2) return reinterpret_cast<float*>(lds_s2);
+      else return reinterpret_cast<float*>(lds_s3);
+    };
+    auto frag_row = [](int v) { return MF == 4 ? v : v / 2; };
+    auto frag_col = [](int v) { return MF == 4 ? 0 : (v % 2) * (NF / 2); };
+    floatx16 fin[1][OWN];
+    __syncthreads();
+    static_for<0, OWN / G>([&](auto pp) __attribute__((always_inline)) {
+      constexpr int PH = decltype(pp)::value;
+      static_for<0, KW>([&](auto vv) __attribute__((always_inline)) {
+        constexpr int V = decltype(vv)::value;
+        if (wave != V) {
+          float* d = obj(vv) + (wave - (wave > V)) * G * (FB / 4);
+          static_for<0, G>([&](auto gg) __attribute__((always_inline)) {
+            constexpr int GI = decltype(gg)::value;
+            const floatx16& a = acc[frag_row(V)][frag_col(V) + PH * G + GI];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) d[(GI * 16 + e) * 64 + lane] = a[e];
+          });
+        }
+      });
+      __syncthreads();
+      static_for<0, KW>([&](auto vv) __attribute__((always_inline)) {
+        constexpr int V = decltype(vv)::value;
+        if (wave == V) {
+          const float* d = obj(vv);
+          static_for<0, G>([&](auto gg) __attribute__((always_inline)) {
+            constexpr int GI = decltype(gg)::value;
+            const floatx16& mine = acc[frag_row(V)][frag_col(V) + PH * G + GI];
+            floatx16 sum;
+            static_for<0, KW>([&](auto ww) __attribute__((always_inline)) {
+              constexpr int W = decltype(ww)::value;
+              floatx16 part;
+              if constexpr (W == V) {
+                part = mine;
+              } else {
+                const float* q = d + (W - (W > V)) * G * (FB / 4) + GI * 16 * 64;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) part[e] = q[e * 64 + lane];
+              }
+              if constexpr (W == 0) sum = part;
+              else sum += part;
+            });
+            fin[0][PH * G + GI] = sum;
+          });
+        }
+      });
+      __syncthreads();
+    });
+    const int fr = frag_row(wave), fc = frag_col(wave);
+    tile_epilogue<1, OWN, 1, 1, false>(fin, ctab + fc * 32, uniform, lane, 0, 0, m0 + fr * 32, cb + fc * 32, m, n,
+                                       out, epi);
+  }
+}
+
+template <int MF, int NF, int WM, int WN, int NSTAGE, bool SILU>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
+                        const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
+                        EpilogueArgs epi, TileMap tmap) {
+  prefill_dma_tile<MF, NF, WM, WN, NSTAGE, SILU, 1>(a_codes, a_scales, m, w_packed, n, k, out, epi, tmap);
+}
+
+// Split-K pieces for a launch's last, partly filled round: KW waves, each
+// over a quarter of K, multiply an MF x NF-fragment piece (a cut tile) with
+// the main kernel's loop, so a piece's K loop is a quarter as long.
+template <int MF, int NF, int NSTAGE, int KW>
+__global__ void __launch_bounds__(KW * 64)
+gemm_prefill_splitk_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m,
+                           const uint8_t* __restrict__ w_packed, int64_t n, int64_t k, void* __restrict__ out,
+                           EpilogueArgs epi, TileMap tmap) {
+  prefill_dma_tile<MF, NF, 1, 1, NSTAGE, false, KW>(a_codes, a_scales, m, w_packed, n, k, out, epi, tmap);
 }
 
 // ------------------------------------------------------------ launcher ----
@@ -826,6 +933,9 @@ gemm_prefill_dma_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __re
 #endif
 #ifndef NVFP4_PREFILL_STAGES
 #define NVFP4_PREFILL_STAGES 4
+#endif
+#ifndef NVFP4_PREFILL_SPLITK
+#define NVFP4_PREFILL_SPLITK 1   // 0: the last round's tiles as cut pieces only
 #endif
 
 // Compute units of the current device (a host-side attribute query).
@@ -904,14 +1014,34 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
       }
     } else {
       NVFP4_LAUNCH_PIECE(MF, NF, false, dim3((unsigned)nbig), big);
-      if constexpr (piece_ok<MF, NF, WM, WN, false>(2, 1))
-        if (ry == 2 && rx == 1) NVFP4_LAUNCH_PIECE(MF / 2, NF, false, tail_grid, tail);
-      if constexpr (piece_ok<MF, NF, WM, WN, false>(2, 2))
-        if (ry == 2 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF / 2, false, tail_grid, tail);
-      if constexpr (piece_ok<MF, NF, WM, WN, false>(4, 2))
-        if (ry == 4 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 4, NF / 2, false, tail_grid, tail);
-      if constexpr (piece_ok<MF, NF, WM, WN, false>(4, 4))
-        if (ry == 4 && rx == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF / 4, false, tail_grid, tail);
+      // Split-K pieces: four waves each take a quarter of K over the whole
+      // piece (pieces of 4x4, 2x2 or 2x4 fragments; K in whole super-tiles,
+      // at least one per wave).  Otherwise the cut pieces split the tile.
+      constexpr int TM = WM * MF, TN = WN * NF;
+      bool sk = false;
+      if constexpr (NS == kSuperTiles && NVFP4_PREFILL_SPLITK) {
+        if (cut && k % kSuperK == 0 && super_count(k) >= 4) {
+#define NVFP4_LAUNCH_SPLITK(MFP, NFP)                                                                    \
+  hipLaunchKernelGGL((gemm_prefill_splitk_kernel<MFP, NFP, NS, 4>), tail_grid, dim3(256), 0, st, ac, as, m, w, n, k, \
+                     out, epi, tail)
+          sk = true;
+          if (TM == 4 * ry && TN == 4 * rx) NVFP4_LAUNCH_SPLITK(4, 4);
+          else if (TM == 2 * ry && TN == 2 * rx) NVFP4_LAUNCH_SPLITK(2, 2);
+          else if (TM == 2 * ry && TN == 4 * rx) NVFP4_LAUNCH_SPLITK(2, 4);
+          else sk = false;
+#undef NVFP4_LAUNCH_SPLITK
+        }
+      }
+      if (!sk) {
+        if constexpr (piece_ok<MF, NF, WM, WN, false>(2, 1))
+          if (ry == 2 && rx == 1) NVFP4_LAUNCH_PIECE(MF / 2, NF, false, tail_grid, tail);
+        if constexpr (piece_ok<MF, NF, WM, WN, false>(2, 2))
+          if (ry == 2 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 2, NF / 2, false, tail_grid, tail);
+        if constexpr (piece_ok<MF, NF, WM, WN, false>(4, 2))
+          if (ry == 4 && rx == 2) NVFP4_LAUNCH_PIECE(MF / 4, NF / 2, false, tail_grid, tail);
+        if constexpr (piece_ok<MF, NF, WM, WN, false>(4, 4))
+          if (ry == 4 && rx == 4) NVFP4_LAUNCH_PIECE(MF / 4, NF / 4, false, tail_grid, tail);
+      }
     }
 #undef NVFP4_LAUNCH_PIECE
   } else if (epi.silu_mul) {

@@ -88,6 +88,11 @@ def test_unit_scales_give_the_exact_integer_product(gpu_lib):
     (512, 35712, 256, "f32"),    # 280 tiles: the last 24 as 8 pieces of 64x128
     (512, 38336, 256, "bf16"),   # 300 tiles: the last 44 as quarters (128x128)
     (512, 46040, 256, "f32"),    # 360 tiles: the last 104 as half-height tiles; ragged N
+    # the same cuts with K in whole weight super-tiles, at least one per wave:
+    # split-K pieces, four waves each over its own quarter of K
+    (512, 33184, 1024, "bf16"),  # 260 tiles: 16 pieces of 2x2 fragments; ragged N
+    (512, 35712, 1280, "f32"),   # 280 tiles: 2x4-fragment pieces, K quarters of 1, 1, 1 and 2 super-tiles
+    (512, 38336, 1024, "bf16"),  # 300 tiles: 4x4-fragment pieces
     # 128x320 tiles (five column fragments per wave), chosen when they need fewer rounds:
     (384, 65617, 256, "bf16"),   # 618 tiles: two rounds, the last 106 as 212 half-height pieces; ragged N
     (2048, 5120, 320, "f32"),    # exactly one round of 256 tiles
