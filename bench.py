@@ -694,7 +694,8 @@ def main():
                    "activations": "quantized per call (dynamic FP32 global scale)"},
         "roofline": {"bound": "mfma",
                      "kernel": "gemm_prefill_dma_kernel (3 GEMMs per step: gdn, gate_up, down; each a full-round "
-                               "launch plus a tail launch)",
+                               "launch plus one for the partly filled last round: split-K pieces, "
+                               "gemm_prefill_splitk_kernel, for gdn and down)",
                      "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": None if traffic is None else int(sum(traffic.values()) / 3),
