@@ -93,6 +93,7 @@ def test_unit_scales_give_the_exact_integer_product(gpu_lib):
     (512, 33184, 1024, "bf16"),  # 260 tiles: 16 pieces of 2x2 fragments; ragged N
     (512, 35712, 1280, "f32"),   # 280 tiles: 2x4-fragment pieces, K quarters of 1, 1, 1 and 2 super-tiles
     (512, 38336, 1024, "bf16"),  # 300 tiles: 4x4-fragment pieces
+    (500, 38336, 1024, "f32"),   # the same with ragged M: the last row band's pieces clamp rows past M
     # 128x320 tiles (five column fragments per wave), chosen when they need fewer rounds:
     (384, 65617, 256, "bf16"),   # 618 tiles: two rounds, the last 106 as 212 half-height pieces; ragged N
     (2048, 5120, 320, "f32"),    # exactly one round of 256 tiles
