@@ -263,6 +263,51 @@ int gemm_w4a4_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
                                 nvfp4_stream_t stream);
 
 /*
+ * nvfp4_silu_amax_parts -- size query: the number of uint32 partial maxima
+ * gemm_w4a4_silu_mul_amax may write for an m x n gate/up projection (0 for
+ * m <= 0 or n <= 0).
+ *
+ * gemm_w4a4_silu_mul_amax -- the MLP gate/up projection with bf16 h (as
+ * gemm_w4a4 with SILU_MUL and bf16 output) that also leaves partial maxima
+ * of |h| for the dynamic global scale of h's on-the-fly quantisation (the
+ * 4-bit activations of W4A4 between the MLP's two GEMMs; bayesiansapien
+ * page, TL;DR).  With nvfp4_quantize_amax_parts this replaces
+ * nvfp4_quantize(h, dynamic_global = 1): the maximum is taken from the values
+ * the GEMM stores, in its epilogue, instead of by a pass that reads h back,
+ * and the codes, scales and global scale are bit-identical to that call's.
+ *
+ *   A, m, w_packed, w_global, n, k as for gemm_w4a4; n % 64 == 0.
+ *   h            bf16 [m, n/2], row stride ld_h (a multiple of 8), 16-byte
+ *                aligned: h = silu(gate) * up, identical to gemm_w4a4's.
+ *   amax_parts   device uint32 [parts_capacity], 4-byte aligned: receives the
+ *                partial maxima (15-bit bf16 magnitude patterns); the buffer
+ *                may be h's codes buffer of the following
+ *                nvfp4_quantize_amax_parts call.
+ *   parts_capacity >= nvfp4_silu_amax_parts(m, n), else NVFP4_ESHAPE.
+ *   parts_written  host int64: the number of partial maxima written (0 for
+ *                m == 0).  Set when the call returns; no device sync.
+ * The prefill kernels (m > 64, k % 64 == 0) write one maximum per wave from
+ * the epilogue; other shapes run gemm_w4a4 and then an amax pass over h.
+ *
+ * nvfp4_quantize_amax_parts -- nvfp4_quantize with dynamic_global = 1 whose
+ * amax is the largest of num_parts partial maxima (from
+ * gemm_w4a4_silu_mul_amax over this x): writes *global_scale = 2688 / amax
+ * (1 if amax == 0), then codes and scales as nvfp4_quantize.
+ *   x, rows, cols, ld_x, global_scale, codes, scales as for nvfp4_quantize.
+ *   amax_parts   device uint32 [num_parts] (4-byte aligned), 1 <= num_parts
+ *                <= 2^31 - 1; may alias codes (the maxima are reduced before
+ *                any code is written).
+ */
+int64_t nvfp4_silu_amax_parts(int64_t m, int64_t n);
+int gemm_w4a4_silu_mul_amax(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t m,
+                            const void* w_packed, const float* w_global, int64_t n, int64_t k, uint16_t* h,
+                            int64_t ld_h, uint32_t* amax_parts, int64_t parts_capacity, int64_t* parts_written,
+                            nvfp4_stream_t stream);
+int nvfp4_quantize_amax_parts(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              const uint32_t* amax_parts, int64_t num_parts, float* global_scale, uint8_t* codes,
+                              uint8_t* scales, nvfp4_stream_t stream);
+
+/*
  * gdn_recurrence -- the gated delta-rule recurrence of a Gated DeltaNet layer,
  * the recurrent half that the in-projection feeds.  The pages characterise
  * it by behaviour rather than by a formula: the delta rule replaces the

@@ -39,6 +39,10 @@ _SIGNATURES = {
                                         _c_p, _c_p, _c_p, _int, _i64, _c_p]),
     "gemm_w4a4_silu_mul_quantize": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p,
                                            _c_p, _c_p]),
+    "nvfp4_silu_amax_parts": (_i64, [_i64, _i64]),
+    "gemm_w4a4_silu_mul_amax": (_int, [_c_p, _c_p, _c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _i64, _c_p, _i64,
+                                       _c_p, _c_p]),
+    "nvfp4_quantize_amax_parts": (_int, [_c_p, _i64, _i64, _i64, _c_p, _i64, _c_p, _c_p, _c_p, _c_p]),
     "gdn_recurrence": (_int, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p, _i64, _i64, _int, _int, _int,
                               _c_p, _c_p, _c_p, _int, _i64, _c_p]),
     "nvfp4_weight_stream_read": (_int, [_c_p, _i64, _i64, _c_p, _c_p]),
@@ -288,6 +292,67 @@ def gemm_w4a4_fused_segments(a_codes, a_scales, a_global, w_packed, n, k, seg_of
                                       _ptr(out), od, _ld(out), _stream())
     _check(rc, "gemm_w4a4_fused_segments")
     return out
+
+
+def nvfp4_silu_amax_parts(m, n):
+    """Entries of the partial-maxima buffer gemm_w4a4_silu_mul_amax needs for an m x n gate/up projection."""
+    return int(load().nvfp4_silu_amax_parts(int(m), int(n)))
+
+
+def gemm_w4a4_silu_mul_amax(a_codes, a_scales, a_global, w_packed, w_global, n, k, h=None, parts=None):
+    """Gate/up GEMM into bf16 h [m, n/2] (silu(gate) * up) that also leaves partial maxima of |h|.
+    Returns (h, parts, n_parts); parts (uint32, allocated if None, at least nvfp4_silu_amax_parts(m, n)
+    entries) may be a view of the codes buffer h is quantised into next (nvfp4_quantize_amax_parts)."""
+    lib = load()
+    _dev(a_codes, torch.uint8, "a_codes")
+    _dev(a_scales, torch.uint8, "a_scales")
+    _dev(a_global, torch.float32, "a_global")
+    _dev(w_packed, torch.uint8, "w_packed")
+    _dev(w_global, torch.float32, "w_global")
+    m = a_codes.shape[0]
+    if a_codes.numel() != m * (k // 2) or a_scales.numel() != m * (k // 16):
+        raise NVFP4Error("a_codes/a_scales do not match [m, k] with k=%d" % k)
+    if w_packed.numel() < nvfp4_packed_weight_bytes(n, k):
+        raise NVFP4Error("w_packed is smaller than the packed size of [%d, %d]" % (n, k))
+    h, _ = _out(h, m, n // 2, torch.bfloat16, a_codes.device)
+    need = nvfp4_silu_amax_parts(m, n)
+    if parts is None:
+        parts = torch.empty(max(need, 1), dtype=torch.int32, device=a_codes.device)
+    if not isinstance(parts, torch.Tensor) or not parts.is_cuda or parts.dtype not in (torch.int32, torch.uint32) \
+            or not parts.is_contiguous():
+        raise NVFP4Error("parts must be a contiguous 32-bit GPU tensor")
+    written = ctypes.c_int64(0)
+    rc = lib.gemm_w4a4_silu_mul_amax(_ptr(a_codes), _ptr(a_scales), _ptr(a_global), m, _ptr(w_packed),
+                                     _ptr(w_global), n, k, _ptr(h), _ld(h), _ptr(parts), parts.numel(),
+                                     ctypes.byref(written), _stream())
+    _check(rc, "gemm_w4a4_silu_mul_amax")
+    return h, parts, int(written.value)
+
+
+def nvfp4_quantize_amax_parts(x, parts, n_parts, global_scale=None, codes=None, scales=None):
+    """nvfp4_quantize with a dynamic global scale whose amax is the largest of n_parts partial maxima
+    (from gemm_w4a4_silu_mul_amax over x).  Returns (codes, scales, g)."""
+    lib = load()
+    _dev(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise NVFP4Error("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if global_scale is None:
+        global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _dev(global_scale, torch.float32, "global_scale")
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+    _dev(codes, torch.uint8, "codes")
+    _dev(scales, torch.uint8, "scales")
+    if not isinstance(parts, torch.Tensor) or not parts.is_cuda or parts.numel() < n_parts:
+        raise NVFP4Error("parts must be a GPU tensor of at least n_parts entries")
+    ld = x.stride(0) if rows > 1 else cols
+    rc = lib.nvfp4_quantize_amax_parts(_ptr(x), rows, cols, ld, _ptr(parts), int(n_parts), _ptr(global_scale),
+                                       _ptr(codes), _ptr(scales), _stream())
+    _check(rc, "nvfp4_quantize_amax_parts")
+    return codes, scales, global_scale
 
 
 def gemm_w4a4_silu_mul_quantize(a_codes, a_scales, a_global, w_packed, w_global, n, k, h_global,

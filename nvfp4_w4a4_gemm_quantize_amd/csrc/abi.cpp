@@ -171,6 +171,31 @@ int gemm_w4a4_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
                                       epi, (hipStream_t)stream));
 }
 
+int64_t nvfp4_silu_amax_parts(int64_t m, int64_t n) { return m > 0 && n > 0 ? silu_amax_parts_bound(m, n) : 0; }
+
+int gemm_w4a4_silu_mul_amax(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t m,
+                            const void* w_packed, const float* w_global, int64_t n, int64_t k, uint16_t* h,
+                            int64_t ld_h, uint32_t* amax_parts, int64_t parts_capacity, int64_t* parts_written,
+                            nvfp4_stream_t stream) {
+  int rc = validate_gemm_silu_amax(a_codes, a_scales, a_global, m, w_packed, w_global, n, k, h, ld_h, amax_parts,
+                                   parts_capacity, m > 0 ? silu_amax_parts_bound(m, n) : 0, parts_written);
+  if (rc) return rc;
+  *parts_written = 0;
+  if (m == 0) return NVFP4_OK;
+  EpilogueArgs epi = plain_epilogue(a_global, w_global, n, true, NVFP4_OUT_BF16, ld_h);
+  return hip_status(launch_gemm_silu_amax(a_codes, a_scales, m, static_cast<const uint8_t*>(w_packed), n, k, h, epi,
+                                          amax_parts, parts_capacity, parts_written, (hipStream_t)stream));
+}
+
+int nvfp4_quantize_amax_parts(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const uint32_t* amax_parts,
+                              int64_t num_parts, float* global_scale, uint8_t* codes, uint8_t* scales,
+                              nvfp4_stream_t stream) {
+  int rc = validate_quantize_parts(x, rows, cols, ld_x, amax_parts, num_parts, global_scale, codes, scales);
+  if (rc || rows == 0) return rc;
+  return hip_status(launch_quantize_from_parts(x, rows, cols, ld_x, amax_parts, num_parts, global_scale, codes, scales,
+                                               (hipStream_t)stream));
+}
+
 int gdn_recurrence(const uint16_t* q, int64_t ld_q, const uint16_t* k, int64_t ld_k, const uint16_t* v, int64_t ld_v,
                    const uint16_t* beta, int64_t ld_beta, const uint16_t* g, int64_t ld_g, int64_t T, int hk, int hv,
                    int head_dim, const float* s_init, float* s_final, void* out, int out_dtype, int64_t ld_out,

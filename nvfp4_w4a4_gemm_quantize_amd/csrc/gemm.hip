@@ -60,10 +60,12 @@ __device__ __forceinline__ bool columns_uniform(const EpilogueArgs& e, int64_t c
 // to bf16 and quantised: a 16-column block of h is split between lanes
 // (r, 0) and (r, 1) (8 values each), which exchange their block maximum and
 // their halves of the codes across the wave halves.
+// Returns (SiLU*mul with epi.h_amax set) the largest |h| this lane stored,
+// as a 15-bit bf16 magnitude pattern; 0 otherwise.
 template <int MF, int NF, int WM, int WN, bool SILU>
-__device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const ColumnEpilogue* ctab, bool uniform,
-                                              int lane, int wave_m, int wave_n, int64_t m0, int64_t col_base,
-                                              int64_t m, int64_t n, void* out, const EpilogueArgs& epi) {
+__device__ __forceinline__ uint32_t tile_epilogue(floatx16 (&acc)[MF][NF], const ColumnEpilogue* ctab, bool uniform,
+                                                  int lane, int wave_m, int wave_n, int64_t m0, int64_t col_base,
+                                                  int64_t m, int64_t n, void* out, const EpilogueArgs& epi) {
   constexpr int NJ = SILU ? NF / 2 : NF;
   const int r = lane & 31, h = lane >> 5;
   const bool bf16 = epi.out_bf16 != 0;
@@ -113,6 +115,8 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const Col
   // the fragment is copied out of the accumulators by compile-time cases.
   const float alpha_u = SILU ? 1.0f / (*epi.a_global * epi.seg_w_global[0]) : (uniform ? ctab[0].alpha : 0.0f);
   const bool quant = SILU && epi.h_codes != nullptr;
+  const bool track = SILU && bf16 && epi.h_amax != nullptr;   // |h| maxima of the stored bf16 values
+  uint32_t hmax = 0;
   const float hg = quant ? *epi.h_global : 0.0f;
   for (int f = 0; f < NJ * MF; ++f) {
     const int jj = f / MF, i = f % MF;
@@ -137,11 +141,19 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const Col
 #pragma unroll
           for (int q = 0; q < 4; ++q) pk[q] = make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
           store_paired(row, c0, pk);
+          if (track && row < m)
+            hmax = max(hmax, max(absmax_bits8(make_uint4(pk[0].x, pk[0].y, pk[1].x, pk[1].y)),
+                                 absmax_bits8(make_uint4(pk[2].x, pk[2].y, pk[3].x, pk[3].y))));
         } else if (row < m) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float w4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
             store4(row, c0 + 8 * q + 4 * h, w4);
+            if (track) {
+#pragma unroll
+              for (int b = 0; b < 4; ++b)     // the bf16 bits store4 wrote (columns past the output excluded)
+                if (c0 + 8 * q + 4 * h + b < ncols) hmax = max(hmax, (uint32_t)f32_to_bf16_rne(w4[b]) & 0x7FFFu);
+            }
           }
         }
         continue;
@@ -213,6 +225,7 @@ __device__ __forceinline__ void tile_epilogue(floatx16 (&acc)[MF][NF], const Col
       }
     }
   }
+  return hmax;
 }
 
 // The lane's two scale pairs (blocks 2h and 2h+1 of a 64-wide K tile) of each
@@ -837,7 +850,14 @@ __device__ __forceinline__ void prefill_dma_tile(const uint8_t* __restrict__ a_c
   const int64_t cb = SILU ? o0 : (int64_t)bx * BN;
   const bool uniform = !SILU && columns_uniform(epi, cb, cb + BN - 1, n);
   if constexpr (!SK) {
-    tile_epilogue<MF, NF, WM, WN, SILU>(acc, ctab, uniform, lane, wave_m, wave_n, m0, cb, m, n, out, epi);
+    const uint32_t hm = tile_epilogue<MF, NF, WM, WN, SILU>(acc, ctab, uniform, lane, wave_m, wave_n, m0, cb, m, n,
+                                                            out, epi);
+    if constexpr (SILU) {
+      if (epi.h_amax != nullptr) {
+        const uint32_t wm = wave_max_u32(hm);
+        if (lane == 0) epi.h_amax[epi.h_amax_base + (int64_t)blockIdx.x * NWAVES + wave] = wm;
+      }
+    }
   } else {
     // Wave v finishes OWN fragments: fragment row v (MF == 4) or half of row
     // v / 2 (MF == 2).  In G-fragment phases every other wave writes its
@@ -956,9 +976,14 @@ constexpr bool piece_ok(int ry, int rx) {
          (!SL || (rx == 1 && NF % 2 == 0));
 }
 
+// amax_written (SiLU*mul with epi.h_amax): receives the number of |h| partial
+// maxima the launches write (one per wave), or 0 when the register-staged
+// kernel runs (it writes none).
 template <int MF, int NF, int WM, int WN>
 static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* w, int64_t n,
-                           int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
+                           int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st,
+                           int64_t* amax_written = nullptr) {
+  if (amax_written) *amax_written = 0;
   constexpr int BM = WM * MF * 32, BN = WN * NF * 32;
   constexpr int NS = NVFP4_PREFILL_STAGES;
   const int64_t cols = epi.silu_mul ? n / 2 : n;
@@ -1001,9 +1026,13 @@ static void launch_prefill(const uint8_t* ac, const uint8_t* as, int64_t m, cons
     const TileMap big{(int)grid.x, (int)grid.y, 0, 1, 1, xcd_chunk};
     const TileMap tail{(int)grid.x, (int)grid.y, (int)nbig, ry, rx, 0};
     const dim3 tail_grid((unsigned)(rem * ry * rx));
+    // the last round's |h| partial maxima follow the full rounds' (same waves per workgroup)
+    EpilogueArgs epi_tail = epi;
+    epi_tail.h_amax_base = epi.h_amax_base + nbig * (WM * WN);
+    if (amax_written) *amax_written = (nbig + (cut ? (int64_t)tail_grid.x : 0)) * (WM * WN);
 #define NVFP4_LAUNCH_PIECE(MFP, NFP, SL, GRID, MAP) \
   hipLaunchKernelGGL((gemm_prefill_dma_kernel<MFP, NFP, WM, WN, NS, SL>), GRID, block, 0, st, ac, as, m, w, n, \
-                     k, out, epi, MAP)
+                     k, out, (MAP).first > 0 ? epi_tail : epi, MAP)
     if (epi.silu_mul) {
       if constexpr (piece_ok<MF, NF, WM, WN, true>(1, 1)) {
         NVFP4_LAUNCH_PIECE(MF, NF, true, dim3((unsigned)nbig), big);
@@ -1060,6 +1089,38 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales, in
                              int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st) {
   launch_prefill<NVFP4_PREFILL_TILE>(a_codes, a_scales, m, w_packed, n, k, out, epi, st);
   return hipGetLastError();
+}
+
+// Partial maxima of |h|: one per wave of the prefill kernels (at most 16
+// pieces of a tile, four waves each), or one per workgroup of an amax pass.
+constexpr int64_t kAmaxPassParts = 1024;
+int64_t silu_amax_parts_bound(int64_t m, int64_t n) {
+  const int64_t tiles = ((m + 255) / 256) * ((n / 2 + 127) / 128);
+  return tiles * 16 * 4 > kAmaxPassParts ? tiles * 16 * 4 : kAmaxPassParts;
+}
+
+hipError_t launch_gemm_silu_amax(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
+                                 int64_t n, int64_t k, uint16_t* h, const EpilogueArgs& epi_in, uint32_t* parts,
+                                 int64_t cap, int64_t* written, hipStream_t st) {
+  *written = 0;
+  if (m > 64) {
+    // prefill kernels: the maxima come from the epilogue
+    EpilogueArgs epi = epi_in;
+    epi.h_amax = parts;
+    epi.h_amax_base = 0;
+    launch_prefill<NVFP4_PREFILL_TILE>(a_codes, a_scales, m, w_packed, n, k, h, epi, st, written);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || *written > 0) return e;
+  } else {
+    const hipError_t e = launch_gemm(a_codes, a_scales, m, w_packed, n, k, h, epi_in, st);
+    if (e != hipSuccess) return e;
+  }
+  // decode and register-staged kernels: an amax pass over h
+  int64_t np = (m * (n / 2) / 8 + 255) / 256;
+  np = np < 1 ? 1 : np > kAmaxPassParts ? kAmaxPassParts : np;
+  np = np > cap ? cap : np;
+  *written = np;
+  return launch_amax_partials(h, m, n / 2, epi_in.ld_out, parts, (int)np, st);
 }
 
 hipError_t launch_linear(const QuantSource& qs, int64_t m, const uint8_t* w_packed, int64_t n, int64_t k,

@@ -34,6 +34,11 @@ struct EpilogueArgs {
   uint8_t* h_codes;
   uint8_t* h_scales;
   uint16_t* h_out;
+  // SiLU*mul with bf16 h output (h_amax != null, prefill kernels): every wave
+  // writes the largest |h| it stored, as a 15-bit bf16 magnitude pattern, to
+  // h_amax[h_amax_base + block * waves + wave].
+  uint32_t* h_amax;
+  int64_t h_amax_base;
 };
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -47,6 +52,21 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, uint8_t* c
                          hipStream_t st);
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
                        int64_t n, int64_t k, void* out, const EpilogueArgs& epi, hipStream_t st);
+// SiLU*mul GEMM into bf16 h [m, n/2] (stride epi.ld_out) that also leaves
+// partial maxima of |h| in parts[0 .. *written): from the prefill kernels'
+// epilogue, or (other paths) from an amax pass over h.  cap >= the bound below.
+hipError_t launch_gemm_silu_amax(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_packed,
+                                 int64_t n, int64_t k, uint16_t* h, const EpilogueArgs& epi, uint32_t* parts,
+                                 int64_t cap, int64_t* written, hipStream_t st);
+int64_t silu_amax_parts_bound(int64_t m, int64_t n);
+// Partial maxima of |x| over a bf16 [rows, cols] (stride ld) into parts[0 .. nparts).
+hipError_t launch_amax_partials(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t* parts,
+                                int nparts, hipStream_t st);
+// Dynamic-scale quantisation whose amax is the maximum of nparts partial maxima
+// (parts may alias codes: they are reduced before any code is written).
+hipError_t launch_quantize_from_parts(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                      const uint32_t* parts, int64_t nparts, float* g, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t st);
 // Gated delta-rule recurrence (head dimension 128): bf16 inputs with row
 // strides in elements, fp32 state [hv, 128, 128], output [T, hv * 128].
 struct GdnArgs {

@@ -235,6 +235,26 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_
   return hipGetLastError();
 }
 
+hipError_t launch_amax_partials(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t* parts,
+                                int nparts, hipStream_t st) {
+  SegmentTable one{};
+  one.num = 1;
+  one.off[0] = 0;
+  one.off[1] = rows;
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(nparts, 1), dim3(kThreads), 0, st, x, cols, ld, one, parts);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_from_parts(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                      const uint32_t* parts, int64_t nparts, float* g, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t st) {
+  hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(kThreads), 0, st, parts, (int)nparts, 1, g);
+  const int64_t nblk = rows * (cols / 16);
+  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(nblk, 8192)), dim3(kThreads), 0, st,
+                     x, rows, cols, ld, g, codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const SegmentTable& segs, float* seg_g,
                        bool dynamic, uint8_t* packed, hipStream_t st) {
   const int64_t np = round_up(n, kTileN), kp = round_up(k, kSuperK);

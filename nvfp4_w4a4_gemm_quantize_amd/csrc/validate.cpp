@@ -88,6 +88,31 @@ int validate_gemm_silu_quantize(const void* a_codes, const void* a_scales, const
   return NVFP4_OK;
 }
 
+int validate_gemm_silu_amax(const void* a_codes, const void* a_scales, const void* a_global, int64_t m,
+                            const void* w_packed, const void* w_global, int64_t n, int64_t k, const void* h,
+                            int64_t ld_h, const void* amax_parts, int64_t parts_capacity, int64_t parts_needed,
+                            const void* parts_written) {
+  if (!parts_written) return NVFP4_EINVAL;
+  if (n <= 0 || n % 64 != 0) return NVFP4_ESHAPE;
+  int rc = validate_gemm_common(a_codes, a_scales, a_global, m, w_packed, n, k, h, NVFP4_OUT_BF16, ld_h, n / 2);
+  if (rc || m == 0) return rc;
+  if (!w_global || !amax_parts) return NVFP4_EINVAL;
+  if (parts_capacity < parts_needed) return NVFP4_ESHAPE;
+  // h is also read with 16-byte loads by the amax pass and the quantizer
+  if (ld_h % 8 != 0 || !aligned16(h) || (reinterpret_cast<uintptr_t>(amax_parts) & 3u)) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+int validate_quantize_parts(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const void* amax_parts,
+                            int64_t num_parts, const void* global_scale, const void* codes, const void* scales) {
+  int rc = validate_quantize(x, rows, cols, ld_x, global_scale, codes, scales);
+  if (rc || rows == 0) return rc;
+  if (!amax_parts) return NVFP4_EINVAL;
+  if (num_parts < 1 || num_parts > INT32_MAX) return NVFP4_ESHAPE;
+  if (reinterpret_cast<uintptr_t>(amax_parts) & 3u) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
 int validate_gdn_recurrence(const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v, int64_t ld_v,
                             const void* beta, int64_t ld_beta, const void* g, int64_t ld_g, int64_t T, int hk,
                             int hv, int head_dim, const void* s_init, const void* s_final, const void* out,

@@ -126,6 +126,26 @@ hipError_t launch_weight_stream_read(const uint8_t*, int64_t n, int64_t k, uint3
   g_call.k = k;
   return hipSuccess;
 }
+int64_t silu_amax_parts_bound(int64_t m, int64_t n) { return m * n / 64 + 1024; }
+hipError_t launch_gemm_silu_amax(const uint8_t*, const uint8_t*, int64_t m, const uint8_t*, int64_t n, int64_t k,
+                                 uint16_t*, const EpilogueArgs& epi, uint32_t*, int64_t, int64_t* written,
+                                 hipStream_t) {
+  record("gemm_silu_amax");
+  g_call.m = m;
+  g_call.n = n;
+  g_call.k = k;
+  g_call.epi = epi;
+  *written = 77;
+  return hipSuccess;
+}
+hipError_t launch_quantize_from_parts(const uint16_t*, int64_t rows, int64_t cols, int64_t, const uint32_t*,
+                                      int64_t nparts, float*, uint8_t*, uint8_t*, hipStream_t) {
+  record("quantize_parts");
+  g_call.rows = rows;
+  g_call.cols = cols;
+  g_call.n = nparts;
+  return hipSuccess;
+}
 hipError_t launch_gdn_recurrence(const GdnArgs& a, hipStream_t) {
   record("gdn");
   g_call.gdn = a;
@@ -265,6 +285,34 @@ int main() {
          NVFP4_EUNSUPPORTED, NONE);
   EXPECT(gdn_recurrence(X, 260, X, 256, X, 768, X, 6, X, 6, 10, 2, 6, 128, nullptr, nullptr, A16, 0, 768, nullptr),
          NVFP4_EALIGN, NONE);
+
+  // gemm_w4a4_silu_mul_amax and nvfp4_quantize_amax_parts
+  {
+    uint16_t* const H = static_cast<uint16_t*>(A16);
+    uint32_t* const P = static_cast<uint32_t*>(A16);
+    const int64_t cap = nvfp4_silu_amax_parts(300, 128);
+    int64_t wr = -1;
+    EXPECT(gemm_w4a4_silu_mul_amax(B, B, G, 300, A16, G, 128, 5120, H, 64, P, cap, &wr, nullptr), 0, "gemm_silu_amax");
+    CHECK(wr == 77 && g_call.m == 300 && g_call.epi.silu_mul == 1 && g_call.epi.out_bf16 == 1 && g_call.epi.ld_out == 64);
+    EXPECT(gemm_w4a4_silu_mul_amax(B, B, G, 300, A16, G, 128, 5120, H, 64, P, cap - 1, &wr, nullptr), NVFP4_ESHAPE,
+           NONE);
+    EXPECT(gemm_w4a4_silu_mul_amax(B, B, G, 300, A16, G, 96, 5120, H, 64, P, cap, &wr, nullptr), NVFP4_ESHAPE, NONE);
+    EXPECT(gemm_w4a4_silu_mul_amax(B, B, G, 300, A16, G, 128, 5120, H, 64, P, cap, nullptr, nullptr), NVFP4_EINVAL,
+           NONE);
+    EXPECT(gemm_w4a4_silu_mul_amax(B, B, G, 300, A16, G, 128, 5120, H, 68, P, cap, &wr, nullptr), NVFP4_EALIGN, NONE);
+    wr = -1;
+    EXPECT(gemm_w4a4_silu_mul_amax(nullptr, nullptr, nullptr, 0, nullptr, nullptr, 128, 5120, nullptr, 64, nullptr, 0,
+                                   &wr, nullptr),
+           0, NONE);
+    CHECK(wr == 0);
+    EXPECT(nvfp4_quantize_amax_parts(H, 300, 64, 64, P, 5, static_cast<float*>(A16), B, B, nullptr), 0,
+           "quantize_parts");
+    CHECK(g_call.rows == 300 && g_call.cols == 64 && g_call.n == 5);
+    EXPECT(nvfp4_quantize_amax_parts(H, 300, 64, 64, P, 0, static_cast<float*>(A16), B, B, nullptr), NVFP4_ESHAPE,
+           NONE);
+    EXPECT(nvfp4_quantize_amax_parts(H, 300, 64, 64, nullptr, 5, static_cast<float*>(A16), B, B, nullptr),
+           NVFP4_EINVAL, NONE);
+  }
 
   // weight stream reference
   EXPECT(nvfp4_weight_stream_read(A16, 17408, 5120, static_cast<uint32_t*>(A16), nullptr), 0, "stream_read");

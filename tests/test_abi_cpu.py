@@ -19,7 +19,7 @@ MIS = 0x10004          # a misaligned one
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int64_t|int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -38,7 +38,8 @@ def test_header_declares_the_four_entry_points_and_helpers():
     fns = declared_functions()
     for name in ("nvfp4_quantize", "nvfp4_e2m1_encode", "nvfp4_pack_weights", "gemm_w4a4", "gemm_w4a4_fused_segments",
                  "nvfp4_linear", "nvfp4_weight_stream_read",
-                 "gemm_w4a4_silu_mul_quantize", "gdn_recurrence", "nvfp4_packed_weight_bytes",
+                 "gemm_w4a4_silu_mul_quantize", "gemm_w4a4_silu_mul_amax", "nvfp4_quantize_amax_parts",
+                 "nvfp4_silu_amax_parts", "gdn_recurrence", "nvfp4_packed_weight_bytes",
                  "nvfp4_unpack_weights_linear",
                  "nvfp4_status_string", "nvfp4_last_hip_error"):
         assert name in fns
@@ -176,6 +177,50 @@ def test_silu_mul_quantize_validation(lib):
     assert sq(lib, hc=0x10008) == EALIGN         # codes rows move as 16-byte-aligned data
     assert sq(lib, ho=MIS) == EALIGN
     assert sq(lib, m=0, ac=None, hc=None) == OK
+
+
+def sa(lib, m=300, n=128, k=128, ac=A16, wg=A16, h=A16, ldh=64, parts=A16, cap=None, wr=True):
+    cap = lib.nvfp4_silu_amax_parts(m, n) if cap is None else cap
+    written = ctypes.c_int64(-7)
+    rc = lib.gemm_w4a4_silu_mul_amax(ac, A16, A16, m, A16, wg, n, k, h, ldh, parts, cap,
+                                     ctypes.byref(written) if wr else None, None)
+    return rc, written.value
+
+
+def test_silu_mul_amax_validation(lib):
+    assert lib.nvfp4_silu_amax_parts(0, 128) == 0
+    assert lib.nvfp4_silu_amax_parts(300, 128) >= 1024              # at least an amax pass's grid
+    assert lib.nvfp4_silu_amax_parts(4096, 34816) == 16 * 136 * 16 * 4   # 64 waves per tile at most
+    assert sa(lib, n=96)[0] == ESHAPE             # gate/up halves: n % 64
+    assert sa(lib, m=-1)[0] == ESHAPE
+    assert sa(lib, k=40)[0] == ESHAPE
+    assert sa(lib, wr=False)[0] == EINVAL          # the count of maxima goes back to the host
+    assert sa(lib, wg=None)[0] == EINVAL
+    assert sa(lib, parts=None)[0] == EINVAL
+    assert sa(lib, h=None)[0] == EINVAL
+    assert sa(lib, cap=1023)[0] == ESHAPE          # below the size query
+    assert sa(lib, ldh=60)[0] == ESHAPE            # shorter than the n/2 columns
+    assert sa(lib, ldh=68)[0] == EALIGN            # h rows are read with 16-byte loads
+    assert sa(lib, h=0x10008)[0] == EALIGN
+    assert sa(lib, parts=0x10002)[0] == EALIGN
+    assert sa(lib, ac=MIS)[0] == EALIGN
+    assert sa(lib, m=0, ac=None, parts=None, h=None) == (OK, 0)
+
+
+def qp(lib, rows=16, cols=64, ld=64, x=A16, parts=A16, np_=4, g=A16, codes=A16, scales=A16):
+    return lib.nvfp4_quantize_amax_parts(x, rows, cols, ld, parts, np_, g, codes, scales, None)
+
+
+def test_quantize_amax_parts_validation(lib):
+    assert qp(lib, cols=40) == ESHAPE
+    assert qp(lib, ld=32) == ESHAPE
+    assert qp(lib, np_=0) == ESHAPE               # a dynamic scale needs at least one maximum
+    assert qp(lib, np_=2 ** 31) == ESHAPE
+    assert qp(lib, parts=None) == EINVAL
+    assert qp(lib, g=None) == EINVAL
+    assert qp(lib, parts=0x10002) == EALIGN
+    assert qp(lib, x=MIS) == EALIGN
+    assert qp(lib, rows=0, x=None, parts=None) == OK
 
 
 def rec(lib, q=A16, ldq=256, k=A16, ldk=256, v=A16, ldv=768, b=A16, ldb=6, g=A16, ldg=6, T=10, hk=2, hv=6, d=128,
